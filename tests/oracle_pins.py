@@ -1,0 +1,414 @@
+"""Pin checks for the CPU oracle.
+
+Each ``check_*`` function compares the oracle against something other than
+itself: a hand-worked fixture, a closed form, a brute-force characterisation,
+a second formulation of the same step, or a published generator output.  The
+checks read the oracle through the module object ``O`` at call time, so the
+mutation tests can plant a mistake in the oracle and confirm a pin fails.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle.moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+class _WL:
+    """Minimal workload record for the oracle's ``forward``."""
+
+    def __init__(self, **kw):
+        self.route = "topk"
+        self.n_groups = 1
+        self.rre_seed = 0
+        self.__dict__.update(kw)
+
+
+# ---------------------------------------------------------------------------
+# worked fixtures
+# ---------------------------------------------------------------------------
+
+def check_worked_fixture(name):
+    g = load_golden(name)
+    wl = _WL(T=g["T"], d_model=g["d_model"], d_ff=g["d_ff"], E=g["E"], k=g["k"],
+             capacity_factor=g["capacity_factor"], act=g["act"])
+    inputs = {"x": np.array(g["x"], np.float32), "w_r": np.array(g["w_r"], np.float32),
+              "bias": None, "group_id": None,
+              "w1": np.array(g["w1"], np.float32), "w2": np.array(g["w2"], np.float32)}
+    r = O.forward(wl, inputs)
+    assert r["capacity"] == g["capacity"]
+    np.testing.assert_array_equal(r["expert_idx"], np.array(g["expert_idx"]))
+    np.testing.assert_allclose(r["gate"], np.array(g["gate"]), rtol=1e-7, atol=0)
+    np.testing.assert_array_equal(r["slot"], np.array(g["slot"]))
+    np.testing.assert_array_equal(r["expert_count"], np.array(g["expert_count"]))
+    np.testing.assert_array_equal(r["slot_token"], np.array(g["slot_token"]))
+    np.testing.assert_allclose(r["y"], np.array(g["y"]), rtol=1e-6, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# capacity
+# ---------------------------------------------------------------------------
+
+def check_capacity_values():
+    # The five layer shapes: (T, E, k, cf) -> capacity, by hand from Eq. 3 with k and ceil.
+    assert O.capacity(512, 8, 1, 1.25) == 80        # 512/8*1.25 = 80
+    assert O.capacity(8192, 128, 1, 1.0) == 64      # 8192/128 = 64
+    assert O.capacity(16384, 64, 2, 2.0) == 1024    # 2*16384/64*2 = 1024
+    assert O.capacity(8192, 64, 1, 1.25) == 160     # 8192/64*1.25 = 160
+    assert O.capacity(32768, 256, 2, 1.25) == 320   # 2*32768/256*1.25 = 320
+    assert O.capacity(10, 4, 1, 1.0) == 3           # 2.5 rounds up
+    assert O.capacity(3, 3, 2, 1.0) == 2
+
+
+def check_capacity_bruteforce(rng):
+    for _ in range(200):
+        T = int(rng.integers(1, 5000))
+        E = int(rng.integers(1, 300))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        cf = float(rng.choice([0.5, 1.0, 1.1, 1.25, 1.5, 2.0, 3.3, 0.07]))
+        need = Fraction(k * T) * Fraction(cf)
+        # smallest integer C with C * E >= k*T*cf, by search
+        C = 0
+        while C * E < need:
+            C += 1
+        assert O.capacity(T, E, k, cf) == C, (T, E, k, cf)
+
+
+# ---------------------------------------------------------------------------
+# router
+# ---------------------------------------------------------------------------
+
+def check_logits_exact(rng):
+    T, d, E = 37, 96, 11
+    xi = rng.integers(-8, 9, size=(T, d))
+    wi = rng.integers(-8, 9, size=(E, d))
+    x = (xi / 8).astype(np.float32)
+    w = (wi / 8).astype(np.float32)
+    h = O.router_logits(x, w)
+    assert h.dtype == np.float32 and h.shape == (T, E)
+    # integer arithmetic: h[t, e] = sum_j xi[t, j] * wi[e, j] / 64
+    ref = np.array([[sum(int(xi[t, j]) * int(wi[e, j]) for j in range(d)) for e in range(E)]
+                    for t in range(T)]) / 64.0
+    np.testing.assert_array_equal(h.astype(np.float64), ref)
+
+
+def check_logits_bias(rng):
+    T, d, E = 9, 16, 7
+    x = (rng.integers(-8, 9, size=(T, d)) / 8).astype(np.float32)
+    w = (rng.integers(-8, 9, size=(E, d)) / 8).astype(np.float32)
+    b = (-1.1 * np.log(np.arange(1, E + 1))).astype(np.float32)
+    h = O.router_logits(x, w, b)
+    for t in range(T):
+        for e in range(E):
+            exact = sum(Fraction(float(x[t, j])) * Fraction(float(w[e, j])) for j in range(d))
+            s = exact + Fraction(float(b[e]))   # fits in float64 exactly
+            assert h[t, e] == np.float32(float(s)), (t, e)
+
+
+def check_softmax(rng):
+    h = rng.normal(size=(50, 9)) * 3
+    p = O.softmax(h)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert (p > 0).all()
+    # two experts: p_0 = 1 / (1 + exp(h_1 - h_0))
+    h2 = rng.normal(size=(20, 2)) * 4
+    p2 = O.softmax(h2)
+    np.testing.assert_allclose(p2[:, 0], 1.0 / (1.0 + np.exp(h2[:, 1] - h2[:, 0])), rtol=1e-14)
+    # equal logits -> uniform; one expert -> 1
+    np.testing.assert_allclose(O.softmax(np.full((3, 5), 2.5)), 0.2, rtol=1e-15)
+    np.testing.assert_array_equal(O.softmax(np.array([[7.0], [-3.0]])), [[1.0], [1.0]])
+    # ratio of two gates = exp of the logit difference (Eq. 1)
+    np.testing.assert_allclose(p[:, 3] / p[:, 5], np.exp(h[:, 3] - h[:, 5]), rtol=1e-12)
+
+
+def check_topk_rank(rng):
+    # logits on a coarse grid to force many ties, plus signed zeros
+    for k in (1, 2, 3):
+        h = (rng.integers(-2, 3, size=(200, 6)) * 0.5).astype(np.float32)
+        h[0] = [0.0, -0.0, 0.0, -0.0, -1.0, -1.0]
+        h[1] = [-0.0, 0.0, -0.5, -0.5, -0.5, -0.0]
+        idx = O.topk(h, k)
+        for t in range(h.shape[0]):
+            assert len(set(idx[t].tolist())) == k
+            for c in range(k):
+                i = idx[t, c]
+                # number of experts that beat i under (larger logit, then lower index)
+                better = sum(1 for j in range(h.shape[1])
+                             if h[t, j] > h[t, i] or (h[t, j] == h[t, i] and j < i))
+                assert better == c, (t, c, h[t], idx[t])
+    assert O.topk(np.array([[0.0, -0.0, 0.0]], np.float32), 2).tolist() == [[0, 1]]
+    assert O.topk(np.array([[-0.0, 0.0]], np.float32), 1).tolist() == [[0]]
+
+
+def check_gate_raw(rng):
+    T, d, E = 40, 8, 5
+    x = (rng.integers(-8, 9, size=(T, d)) / 8).astype(np.float32)
+    w = (rng.integers(-8, 9, size=(E, d)) / 8).astype(np.float32)
+    idx, gate, h = O.route_topk(x, w, None, 2)
+    hh = h.astype(np.float64)
+    for t in range(T):
+        z = sum(math.exp(v) for v in hh[t])
+        for c in range(2):
+            assert abs(float(gate[t, c]) - math.exp(hh[t, idx[t, c]]) / z) <= 1e-7 * gate[t, c]
+        assert gate[t, 0] >= gate[t, 1]
+
+
+def check_splitmix_reference():
+    g = load_golden("splitmix64_reference.json")
+    got = O.splitmix64(g["seed"], len(g["outputs_hex"]))
+    assert [int(h, 16) for h in g["outputs_hex"]] == got
+
+
+def check_rre(rng):
+    E, G, T = 64, 4, 20000
+    gid = rng.integers(0, G, size=T).astype(np.int32)
+    idx, gate = O.route_rre(gid, E, G, seed=12345)
+    size = E // G
+    assert idx.shape == (T, 1) and (gate == 1.0).all()
+    assert ((idx[:, 0] // size) == gid).all()
+    # uniform within the group: chi-square over the 16 members of each group
+    for g in range(G):
+        members = idx[gid == g, 0] - g * size
+        counts = np.bincount(members, minlength=size)
+        exp = len(members) / size
+        chi2 = float(((counts - exp) ** 2 / exp).sum())
+        assert chi2 < 45.0, chi2       # 15 dof, p ~ 1e-4
+    # the pick for token t is the t-th SplitMix64 output (not shifted by a token)
+    r = O.splitmix64(7, 5)
+    idx2, _ = O.route_rre(np.zeros(5, np.int32), 8, 1, seed=7)
+    assert idx2[:, 0].tolist() == [v % 8 for v in r]
+    bad, gbad = O.route_rre(np.array([0, 4, -1], np.int32), 8, 4, 0)
+    assert bad[1, 0] == -1 and bad[2, 0] == -1 and gbad[1, 0] == 0.0
+
+
+# ---------------------------------------------------------------------------
+# dispatch
+# ---------------------------------------------------------------------------
+
+def onehot_dispatch(expert_idx, E, C):
+    """Second formulation: one-hot dispatch masks with cumulative sums.
+
+    Position of each assignment in its expert's buffer = number of earlier
+    assignments to that expert, counted with a cumulative sum over tokens for
+    each choice, offset by the totals of all earlier choices.  Returns the
+    dense dispatch tensor D[t, e, c] (0/1) of shape [T, E, C] plus slot.
+    """
+    T, k = expert_idx.shape
+    D = np.zeros((T, E, C), np.int64)
+    slot = np.full((T, k), -1, np.int64)
+    offset = np.zeros(E, np.int64)
+    for c in range(k):
+        valid = (expert_idx[:, c] >= 0) & (expert_idx[:, c] < E)
+        m = np.zeros((T, E), np.int64)
+        m[np.nonzero(valid)[0], expert_idx[valid, c]] = 1
+        pos = np.cumsum(m, axis=0) - 1 + offset[None, :]
+        keep = (m == 1) & (pos < C)
+        tt, ee = np.nonzero(keep)
+        D[tt, ee, pos[tt, ee]] = 1
+        slot[tt, c] = pos[tt, ee]
+        offset += m.sum(axis=0)
+    return D, slot
+
+
+def check_dispatch_invariants(rng):
+    for trial in range(60):
+        T = int(rng.integers(1, 300))
+        E = int(rng.integers(1, 12))
+        k = int(rng.integers(1, min(E, 3) + 1))
+        C = int(rng.integers(1, 2 * T // max(E, 1) + 3))
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        if trial % 5 == 0:
+            idx[rng.random(T) < 0.1, 0] = -1
+        slot, count, slot_token = O.dispatch(idx, E, C)
+        assert (count <= C).all()
+        valid = ((idx >= 0) & (idx < E)).sum()
+        assert count.sum() + ((slot < 0) & (idx >= 0)).sum() == valid
+        for e in range(E):
+            served = [(t, c) for c in range(k) for t in range(T) if idx[t, c] == e and slot[t, c] >= 0]
+            assert len(served) == count[e]
+            for t, c in served:
+                assert slot_token[e, slot[t, c]] == t
+            assert (slot_token[e, count[e]:] == -1).all()
+        D, slot2 = onehot_dispatch(idx, E, C)
+        np.testing.assert_array_equal(slot, slot2)
+
+
+def check_dispatch_no_drop(rng):
+    # capacity factor >= E/k makes capacity >= T: every token is served
+    for _ in range(20):
+        T = int(rng.integers(1, 200))
+        E = int(rng.integers(2, 10))
+        k = int(rng.integers(1, 3))
+        cf = E / k
+        C = O.capacity(T, E, k, cf)
+        assert C >= T
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        slot, count, _ = O.dispatch(idx, E, C)
+        assert (slot >= 0).all() and count.sum() == k * T
+
+
+def check_choice_priority(rng):
+    # a second choice is never served by an expert that dropped a first choice
+    for _ in range(30):
+        T, E, C = 120, 4, int(rng.integers(10, 40))
+        idx = np.stack([rng.permutation(E)[:2] for _ in range(T)]).astype(np.int32)
+        slot, count, _ = O.dispatch(idx, E, C)
+        for e in range(E):
+            dropped_first = ((idx[:, 0] == e) & (slot[:, 0] < 0)).any()
+            if dropped_first:
+                assert not ((idx[:, 1] == e) & (slot[:, 1] >= 0)).any()
+
+
+# ---------------------------------------------------------------------------
+# FFN and combine
+# ---------------------------------------------------------------------------
+
+def check_gelu_values():
+    z = np.array([0.0, 1.0, -1.0, 2.0, -3.0])
+    g = O.act_fn(z, "gelu")
+    # Phi(1) = 0.8413447460685429 (standard normal CDF, textbook value)
+    np.testing.assert_allclose(g[:3], [0.0, 0.8413447460685429, -0.15865525393145707], rtol=1e-14)
+    # GELU(z) - GELU(-z) = z  (since Phi(z) + Phi(-z) = 1)
+    zz = np.linspace(-6, 6, 101)
+    np.testing.assert_allclose(O.act_fn(zz, "gelu") - O.act_fn(-zz, "gelu"), zz, atol=1e-14)
+    np.testing.assert_array_equal(O.act_fn(np.array([-2.0, 0.0, 3.5]), "relu"), [0.0, 0.0, 3.5])
+
+
+def _rand_layer(rng, T, d, f, E, k, cf, act, zipf=False, ties=False):
+    wl = _WL(T=T, d_model=d, d_ff=f, E=E, k=k, capacity_factor=cf, act=act)
+    x = (rng.integers(-8, 9, size=(T, d)) / 8).astype(np.float32)
+    w_r = (rng.integers(-8, 9, size=(E, d)) / 8).astype(np.float32)
+    if not ties:
+        # break every tie: distinct per-expert offsets far below the 1/64 grid
+        bias = (np.arange(E) * 2.0 ** -12).astype(np.float32)
+    else:
+        bias = None
+    if zipf:
+        bias = (-1.1 * np.log(np.arange(1, E + 1))).astype(np.float32)
+    w1 = (rng.normal(size=(E, f, d)) / math.sqrt(d)).astype(np.float32)
+    w2 = (rng.normal(size=(E, d, f)) / math.sqrt(f)).astype(np.float32)
+    return wl, {"x": x, "w_r": w_r, "bias": bias, "group_id": None, "w1": w1, "w2": w2}
+
+
+def dense_layer(wl, inputs, r):
+    """Dense brute force: every expert on every token, masked by the served choices.
+
+    Built from the one-hot dispatch tensor D and the combine tensor gate * D,
+    evaluated with einsum over [T, E, C] (the dispatch/combine tensor form of
+    Switch notes 2.4).
+    """
+    x = O.as_f64(inputs["x"])
+    D, _ = onehot_dispatch(r["expert_idx"], wl.E, r["capacity"])
+    Wc = np.zeros(D.shape)
+    T, k = r["expert_idx"].shape
+    for t in range(T):
+        for c in range(k):
+            e = r["expert_idx"][t, c]
+            if 0 <= e < wl.E:
+                Wc[t, e] += float(r["gate"][t, c]) * D[t, e]
+    xe = np.einsum("tec,td->ecd", D, x)
+    w1 = O.as_f64(inputs["w1"])
+    w2 = O.as_f64(inputs["w2"])
+    hid = O.act_fn(np.einsum("ecd,efd->ecf", xe, w1), wl.act)
+    ye = np.einsum("ecf,edf->ecd", hid, w2)
+    return np.einsum("tec,ecd->td", Wc, ye)
+
+
+def check_dense_equals_sparse(rng):
+    for (T, d, f, E, k, cf, act, zipf) in [(64, 16, 24, 4, 1, 1.0, "relu", False),
+                                           (90, 8, 12, 6, 2, 1.0, "gelu", False),
+                                           (50, 16, 8, 5, 2, 0.5, "gelu", True),
+                                           (33, 8, 8, 3, 3, 1.0, "relu", False)]:
+        wl, inp = _rand_layer(rng, T, d, f, E, k, cf, act, zipf)
+        r = O.forward(wl, inp)
+        np.testing.assert_allclose(r["y"], dense_layer(wl, inp, r), rtol=1e-12, atol=1e-12)
+
+
+def check_single_expert_is_mlp(rng):
+    import torch
+    T, d, f = 30, 12, 20
+    for act in ("relu", "gelu"):
+        wl, inp = _rand_layer(rng, T, d, f, 1, 1, 1.0, act, ties=True)
+        inp["bias"] = None
+        r = O.forward(wl, inp)
+        assert (r["gate"] == 1.0).all() and (r["slot"][:, 0] == np.arange(T)).all()
+        xt = torch.tensor(inp["x"], dtype=torch.float64)
+        l1 = torch.nn.Linear(d, f, bias=False, dtype=torch.float64)
+        l2 = torch.nn.Linear(f, d, bias=False, dtype=torch.float64)
+        with torch.no_grad():
+            l1.weight.copy_(torch.tensor(inp["w1"][0], dtype=torch.float64))
+            l2.weight.copy_(torch.tensor(inp["w2"][0], dtype=torch.float64))
+            a = torch.relu if act == "relu" else (lambda z: torch.nn.functional.gelu(z, approximate="none"))
+            ref = l2(a(l1(xt))).numpy()
+        np.testing.assert_allclose(r["y"], ref, rtol=1e-12, atol=1e-13)
+
+
+def check_k_equals_E_is_softmax_mixture(rng):
+    T, d, f, E = 25, 8, 10, 4
+    wl, inp = _rand_layer(rng, T, d, f, E, E, float(E), "gelu")
+    r = O.forward(wl, inp)
+    assert (r["slot"] >= 0).all()
+    x = O.as_f64(inp["x"])
+    h = x @ O.as_f64(inp["w_r"]).T + O.as_f64(inp["bias"])
+    p = np.exp(h) / np.exp(h).sum(axis=1, keepdims=True)
+    ref = np.zeros((T, d))
+    for e in range(E):
+        z = x @ O.as_f64(inp["w1"][e]).T
+        g = z * 0.5 * (1 + np.vectorize(math.erf)(z / math.sqrt(2)))
+        ref += p[:, e:e + 1] * (g @ O.as_f64(inp["w2"][e]).T)
+    # gates are float32, so agreement is to float32 rounding
+    np.testing.assert_allclose(r["y"], ref, rtol=2e-7 * 4, atol=1e-7)
+
+
+def check_expert_permutation(rng):
+    T, d, f, E, k = 80, 16, 12, 6, 2
+    wl, inp = _rand_layer(rng, T, d, f, E, k, 1.25, "gelu", ties=True)
+    # distinct offsets far below the 1/64 logit grid make every row tie-free, so
+    # the lowest-index tie rule never applies and relabelling is exact
+    inp["bias"] = (rng.permutation(E) * 2.0 ** -12).astype(np.float32)
+    r = O.forward(wl, inp)
+    assert (np.diff(np.sort(r["logits"], axis=1), axis=1) != 0).all()
+    perm = rng.permutation(E)           # new expert j is old expert perm[j]
+    inv = np.argsort(perm)
+    inp2 = dict(inp)
+    for key in ("w_r", "bias", "w1", "w2"):
+        inp2[key] = inp[key][perm]
+    r2 = O.forward(wl, inp2)
+    np.testing.assert_array_equal(r2["expert_idx"], inv[r["expert_idx"]])
+    np.testing.assert_array_equal(r2["expert_count"], r["expert_count"][perm])
+    np.testing.assert_array_equal(r2["slot"], r["slot"])
+    np.testing.assert_allclose(r2["y"], r["y"], rtol=1e-13, atol=1e-13)
+
+
+def check_aux_loss(rng):
+    # uniform routing: f_i = P_i = 1/N -> loss = alpha (Switch notes 2.2 after Eq. 6)
+    N = 8
+    # all-equal logits: p_i = 1/N; every argmax ties to expert 0, f = (1, 0, ..., 0),
+    # so loss = alpha * N * (1 * 1/N) = alpha
+    logits = np.zeros((N * 5, N), np.float32)
+    assert abs(O.aux_loss(logits) - 1e-2) < 1e-15
+    # balanced argmax with near-uniform probabilities
+    eps = 2.0 ** -30
+    lg = np.zeros((N * 4, N))
+    for t in range(N * 4):
+        lg[t, t % N] = eps
+    assert abs(O.aux_loss(lg, alpha=1.0) - 1.0) < 1e-6
+    # hand-worked: N=2, tokens with logits [0, ln 3] and [0, 0]:
+    # p = (1/4, 3/4) and (1/2, 1/2); f = (1/2, 1/2) (second row ties -> expert 0);
+    # P = (3/8, 5/8); loss = alpha * 2 * (1/2*3/8 + 1/2*5/8) = alpha
+    lg2 = np.array([[0.0, math.log(3.0)], [0.0, 0.0]])
+    assert abs(O.aux_loss(lg2, alpha=1.0) - 1.0) < 1e-12
+    # all tokens to expert 1 with p_1 = 3/4: f = (0, 1), P = (1/4, 3/4) -> 2 * 3/4 = 1.5
+    lg3 = np.array([[0.0, math.log(3.0)]] * 3)
+    assert abs(O.aux_loss(lg3, alpha=1.0) - 1.5) < 1e-12

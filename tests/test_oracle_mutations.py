@@ -1,0 +1,161 @@
+"""Planted mistakes: each plausible error in the oracle must make at least one pin fail.
+
+The mistakes are planted in the oracle (on the CPU, through monkeypatch), never in
+any GPU code.  A mutation "survives" if every listed pin still passes.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as O
+import oracle_pins as P
+
+_orig = {n: getattr(O, n) for n in dir(O) if callable(getattr(O, n))}
+
+
+def _cap_no_k(T, E, k, cf):
+    return _orig["capacity"](T, E, 1, cf)
+
+
+def _cap_floor(T, E, k, cf):
+    from fractions import Fraction
+    return int(math.floor(Fraction(k * T) * Fraction(cf) / E))
+
+
+def _logits_no_bias(x, w_r, bias=None):
+    return _orig["router_logits"](x, w_r, None)
+
+
+def _logits_bias_in_f64(x, w_r, bias=None):
+    h = O.as_f64(x) @ O.as_f64(w_r).T
+    if bias is not None:
+        h = h + np.asarray(bias, np.float64) * (1 + 2.0 ** -30)
+    return h.astype(np.float32)
+
+
+def _softmax_unnormalised(h):
+    h = np.asarray(h, np.float64)
+    return np.exp(h - h.max(axis=-1, keepdims=True))
+
+
+def _topk_high_index_ties(h, k):
+    h = np.asarray(h)
+    E = h.shape[1]
+    rev = _orig["topk"](h[:, ::-1], k)
+    return (E - 1 - rev).astype(np.int32)
+
+
+def _topk_smallest(h, k):
+    return _orig["topk"](-np.asarray(h), k)
+
+
+def _route_topk_renorm(x, w_r, bias, k):
+    idx, gate, h = _orig["route_topk"](x, w_r, bias, k)
+    g = gate.astype(np.float64)
+    return idx, (g / g.sum(axis=1, keepdims=True)).astype(np.float32), h
+
+
+def _dispatch_token_major(expert_idx, E, C):
+    T, k = expert_idx.shape
+    slot = np.full((T, k), -1, np.int32)
+    count = np.zeros(E, np.int64)
+    st = np.full((E, C), -1, np.int32)
+    for t in range(T):
+        for c in range(k):
+            e = int(expert_idx[t, c])
+            if 0 <= e < E and count[e] < C:
+                slot[t, c] = count[e]
+                st[e, count[e]] = t
+                count[e] += 1
+    return slot, count.astype(np.int32), st
+
+
+def _dispatch_overfill(expert_idx, E, C):
+    # off by one: lets each expert take C+1 assignments
+    s, c, st = _orig["dispatch"](expert_idx, E, C + 1)
+    return s, c, st[:, :C]
+
+
+def _combine_no_gate(y_e, expert_idx, slot, gate, d_model):
+    return _orig["combine"](y_e, expert_idx, slot, np.ones_like(gate), d_model)
+
+
+def _combine_first_gate(y_e, expert_idx, slot, gate, d_model):
+    g = np.repeat(gate[:, :1], gate.shape[1], axis=1)
+    return _orig["combine"](y_e, expert_idx, slot, g, d_model)
+
+
+def _act_tanh_gelu(z, act):
+    if act == "gelu":
+        return 0.5 * z * (1 + np.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)))
+    return _orig["act_fn"](z, act)
+
+
+def _expert_apply_w2_untransposed(xrows, w1_e, w2_e, act):
+    hdn = O.act_fn(xrows @ O.as_f64(w1_e).T, act)
+    w2 = O.as_f64(w2_e)
+    return hdn @ w2.reshape(w2.shape[1], w2.shape[0])
+
+
+def _splitmix_bad_shift(seed, n):
+    out, state, M = [], seed, (1 << 64) - 1
+    for _ in range(n):
+        state = (state + 0x9E3779B97F4A7C15) & M
+        z = state
+        z = ((z ^ (z >> 31)) * 0xBF58476D1CE4E5B9) & M
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M
+        out.append(z ^ (z >> 31))
+    return out
+
+
+def _rre_shifted(group_id, E, n_groups, seed):
+    T = len(group_id)
+    r = O.splitmix64(seed, T + 1)[1:]
+    size = E // n_groups
+    idx = np.array([[int(g) * size + v % size] for g, v in zip(group_id, r)], np.int32)
+    return idx, np.ones((T, 1), np.float32)
+
+
+ALL_PINS = [
+    lambda rng: P.check_worked_fixture("switch_top1_worked.json"),
+    lambda rng: P.check_worked_fixture("top2_priority_worked.json"),
+    lambda rng: P.check_capacity_values(),
+    P.check_capacity_bruteforce, P.check_logits_exact, P.check_logits_bias, P.check_softmax,
+    P.check_topk_rank, P.check_gate_raw, lambda rng: P.check_splitmix_reference(), P.check_rre,
+    P.check_dispatch_invariants, P.check_dispatch_no_drop, P.check_choice_priority,
+    lambda rng: P.check_gelu_values(), P.check_dense_equals_sparse, P.check_single_expert_is_mlp,
+    P.check_k_equals_E_is_softmax_mixture, P.check_expert_permutation, P.check_aux_loss,
+]
+
+MUTATIONS = {
+    "capacity_without_k": ("capacity", _cap_no_k),
+    "capacity_floor": ("capacity", _cap_floor),
+    "logits_drop_bias": ("router_logits", _logits_no_bias),
+    "logits_bias_rounded_wrong": ("router_logits", _logits_bias_in_f64),
+    "softmax_unnormalised": ("softmax", _softmax_unnormalised),
+    "topk_ties_to_high_index": ("topk", _topk_high_index_ties),
+    "topk_smallest": ("topk", _topk_smallest),
+    "gates_renormalised": ("route_topk", _route_topk_renorm),
+    "dispatch_token_major": ("dispatch", _dispatch_token_major),
+    "dispatch_overfill": ("dispatch", _dispatch_overfill),
+    "combine_without_gate": ("combine", _combine_no_gate),
+    "combine_wrong_choice_gate": ("combine", _combine_first_gate),
+    "gelu_tanh_approximation": ("act_fn", _act_tanh_gelu),
+    "w2_not_transposed": ("expert_apply", _expert_apply_w2_untransposed),
+    "splitmix_wrong_shift": ("splitmix64", _splitmix_bad_shift),
+    "rre_off_by_one_token": ("route_rre", _rre_shifted),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = 0
+    for pin in ALL_PINS:
+        try:
+            pin(np.random.default_rng(7))
+        except Exception:  # an assertion or a shape error both expose the mistake
+            caught += 1
+    assert caught > 0, f"planted mistake {name} survived every pin"
