@@ -1,0 +1,184 @@
+/*
+ * moe.h -- C ABI of the sparse Mixture-of-Experts layer forward pass on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer maps token representations x [T, d_model] to y [T, d_model]:
+ *   1. router   : logits h(x) = W_r . x, gates p = softmax(h), top-k experts
+ *                 (Switch Transformers notes, section 2.1, Eq. 1; top-1 Switch
+ *                 routing; top-2 X-MoE routing from the TorchScale review), or a
+ *                 weightless uniform pick inside the token's expert group
+ *                 (PanGu-Sigma review, Random Routed Experts);
+ *   2. dispatch : capacity-limited slot assignment (Switch notes, section 2.2,
+ *                 Eq. 3 and the token-dropping rule);
+ *   3. gather   : rows of x copied into an expert-major buffer;
+ *   4. experts  : y_e = act(x_e W1_e) W2_e per expert;
+ *   5. combine  : y = sum over the token's served choices of p_i(x) E_i(x)
+ *                 (Switch notes, section 2.1, Eq. 2).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named x, w_r, bias, group_id, w1, w2, y, expert_idx, gate, slot,
+ *     expert_count, slot_token, x_e, y_e and ws are DEVICE pointers owned by the
+ *     caller.  The library allocates nothing and keeps no state between calls.
+ *     `cfg` is a HOST pointer, read during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All GPU work is enqueued on it; no call synchronises the host.  Results
+ *     are valid once the caller has synchronised the stream.
+ *   - Return value: MOE_OK, or a negative status.  On MOE_ERR_ARG and
+ *     MOE_ERR_UNSUPPORTED nothing was launched and no output was touched;
+ *     moe_last_error() returns a message (thread-local, valid until the next
+ *     call on the same thread).  MOE_ERR_HIP means a HIP launch failed;
+ *     outputs are then undefined.  Faults inside kernels surface at the
+ *     caller's next synchronisation, as for any HIP work.
+ *   - All buffers must be 16-byte aligned (torch allocations are 256-byte).
+ *   - Shapes are row-major, last index contiguous.  "dtype" below means
+ *     cfg->dtype: MOE_DTYPE_BF16 (raw bfloat16) or MOE_DTYPE_F32.
+ *   - Supported sizes: T >= 0; 1 <= E <= 512; 1 <= k <= min(E, 8);
+ *     d_model and d_ff positive multiples of 64; capacity_factor finite > 0;
+ *     RRE needs k == 1, n_groups >= 1 and E % n_groups == 0.
+ *   - Calls that share a workspace must not overlap in time (same stream, or
+ *     ordered by events).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 } moe_act;
+typedef enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_RRE = 1 } moe_route;
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,          /* a null pointer, a bad enum or an inconsistent size */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid configuration outside the supported sizes */
+  MOE_ERR_HIP = -3           /* a HIP runtime call or kernel launch failed */
+};
+
+typedef struct moe_config {
+  int64_t T;               /* tokens in the call (all sequences flattened)          */
+  int64_t d_model;         /* token width                                            */
+  int64_t d_ff;            /* expert hidden width                                    */
+  int32_t E;               /* experts                                                */
+  int32_t k;               /* expert choices per token                               */
+  double capacity_factor;  /* Switch notes 2.2, Eq. 3                                */
+  int32_t route;           /* moe_route                                              */
+  int32_t n_groups;        /* RRE: expert groups (experts g*E/n_groups ... next)     */
+  uint64_t rre_seed;       /* RRE: SplitMix64 seed                                   */
+  int32_t act;             /* moe_act: ReLU, or GELU with the exact erf              */
+  int32_t dtype;           /* moe_dtype of x, w1, w2, x_e, y_e, y                    */
+} moe_config;
+
+/* Expert capacity C = ceil(k * T * capacity_factor / E), evaluated exactly on
+ * the binary value of capacity_factor (Switch notes 2.2, Eq. 3; each token
+ * takes k slots, and the fraction rounds up).  Returns C >= 0, or a negative
+ * status for an invalid configuration. */
+int64_t moe_capacity(const moe_config* cfg);
+
+/* Bytes of device workspace every entry point below needs (`ws`).  It holds
+ * the step-wise scratch (router histograms, slot offsets, the split router
+ * weight, the expert hidden activations) and, for moe_forward, every
+ * intermediate result at the offsets of moe_workspace_offset.  Negative status
+ * on an invalid configuration. */
+int64_t moe_workspace_bytes(const moe_config* cfg);
+
+/* Regions of the workspace that moe_forward fills, for inspection after the call. */
+typedef enum {
+  MOE_WS_EXPERT_IDX = 0,   /* int32 [T, k]                                   */
+  MOE_WS_GATE = 1,         /* float [T, k]                                   */
+  MOE_WS_SLOT = 2,         /* int32 [T, k]                                   */
+  MOE_WS_EXPERT_COUNT = 3, /* int32 [E]                                      */
+  MOE_WS_SLOT_TOKEN = 4,   /* int32 [E, C]                                   */
+  MOE_WS_X_E = 5,          /* dtype [E, C, d_model]                          */
+  MOE_WS_HIDDEN = 6,       /* dtype [E, C, d_ff]  act(x_e W1) per expert     */
+  MOE_WS_Y_E = 7,          /* dtype [E, C, d_model]                          */
+  MOE_WS_N_REGIONS = 8
+} moe_ws_region;
+
+/* Byte offset of a region inside the workspace (256-byte aligned), or a
+ * negative status. */
+int64_t moe_workspace_offset(const moe_config* cfg, int32_t region);
+
+/* Step 1, router.  Switch notes 2.1 (logits h = W_r . x, Eq. 1 softmax gate,
+ * top-k set) and 2.4 (router arithmetic in float32); TorchScale review (X-MoE
+ * top-1/top-2); PanGu-Sigma review (RRE).
+ *   x          [T, d_model] dtype
+ *   w_r        [E, d_model] float32 (learned routing; ignored for RRE)
+ *   bias       [E] float32 or NULL: added to each logit after the dot product,
+ *              with one float32 rounding
+ *   group_id   [T] int32 (RRE only; NULL for learned routing)
+ *   expert_idx [T, k] int32 out: column c is the (c+1)-th choice; larger logit
+ *              first, equal logits to the lower expert index.  RRE: expert
+ *              g*(E/n_groups) + (SplitMix64 output t for rre_seed) mod
+ *              (E/n_groups); a group id outside [0, n_groups) gives -1.
+ *   gate       [T, k] float32 out: raw softmax probability of the chosen
+ *              expert over all E (no renormalisation); RRE: 1 (0 for -1).
+ *   ws         workspace of moe_workspace_bytes(cfg) bytes (scratch).
+ * The logits are computed in float32 arithmetic (bf16 x is widened exactly;
+ * the float32 w_r is split into three bfloat16 terms when it is not already
+ * bfloat16-exact, so each product is exact). */
+int moe_router(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
+               const int32_t* group_id, int32_t* expert_idx, float* gate, void* ws,
+               void* stream);
+
+/* Steps 2 and 3, capacity-limited dispatch and gather.  Switch notes 2.2
+ * (Eq. 3 capacity; an assignment to a full expert is dropped).
+ * Assignments are placed choice by choice and, inside a choice, in token
+ * order: every first choice takes its slot before any second choice.
+ *   x            [T, d_model] dtype
+ *   expert_idx   [T, k] int32; entries outside [0, E) are not routed
+ *   slot         [T, k] int32 out: slot in the expert's buffer, -1 if dropped
+ *   expert_count [E] int32 out: filled slots per expert (<= C)
+ *   slot_token   [E, C] int32 out: token of each slot, -1 where empty
+ *   x_e          [E, C, d_model] dtype out: x_e[e, s] = x[slot_token[e, s]] for
+ *                s < expert_count[e]; rows past the count are not written.
+ *   ws           workspace (scratch). */
+int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* expert_idx, int32_t* slot,
+                 int32_t* expert_count, int32_t* slot_token, void* x_e, void* ws, void* stream);
+
+/* Step 4, expert FFN.  Switch notes 2.1 (one FFN E_i per expert):
+ * y_e[e, s] = act(x_e[e, s] W1_e) W2_e for s < expert_count[e], with
+ * W1_e = w1[e]^T and W2_e = w2[e]^T.
+ *   x_e          [E, C, d_model] dtype (rows past the count are never read)
+ *   expert_count [E] int32 (values above C are treated as C)
+ *   w1           [E, d_ff, d_model] dtype (stored output x input)
+ *   w2           [E, d_model, d_ff] dtype (stored output x input)
+ *   y_e          [E, C, d_model] dtype out (rows past the count are not written)
+ *   ws           workspace: the hidden activations act(x_e W1) in dtype.
+ * bf16: matrix products on bf16 MFMA with float32 accumulation; the hidden
+ * activation and y_e are rounded to bf16.  f32: float32 throughout. */
+int moe_expert_ffn(const moe_config* cfg, const void* x_e, const int32_t* expert_count,
+                   const void* w1, const void* w2, void* y_e, void* ws, void* stream);
+
+/* Step 5, combine.  Switch notes 2.1, Eq. 2: y[t] = sum over c with
+ * slot[t, c] >= 0 of gate[t, c] * y_e[expert_idx[t, c], slot[t, c]],
+ * accumulated in float32 in choice order; a token with no served choice gets
+ * y[t] = 0 (Switch notes 2.2: it continues through the residual, which is the
+ * caller's).
+ *   y_e [E, C, d_model] dtype; expert_idx, slot [T, k] int32; gate [T, k] float;
+ *   y   [T, d_model] dtype out. */
+int moe_combine(const moe_config* cfg, const void* y_e, const int32_t* expert_idx,
+                const int32_t* slot, const float* gate, void* y, void* stream);
+
+/* The whole layer, steps 1-5, on one stream.  Same arguments and results as
+ * the step-wise calls; every intermediate is left in `ws` at the offsets of
+ * moe_workspace_offset.  Capacity comes from the configuration alone, so no
+ * device-to-host copy happens anywhere. */
+int moe_forward(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
+                const int32_t* group_id, const void* w1, const void* w2, void* y, void* ws,
+                void* stream);
+
+/* Message of the last non-OK status on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

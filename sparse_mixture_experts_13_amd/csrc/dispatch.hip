@@ -1,0 +1,166 @@
+// Capacity-limited dispatch and gather (Switch Transformers notes, section 2.2:
+// expert capacity, Eq. 3; an assignment that finds its expert full is dropped).
+//
+// Order: assignments are placed choice by choice and, inside a choice, in token
+// order, so the slot of (token t, choice c) in expert e is the number of earlier
+// assignments to e in that order.  Computed without atomics on global memory in
+// three phases over blocks of 64 tokens (the router's blocks):
+//   1. per-block histogram hist[e][c][b] (the router epilogue writes it; the
+//      stand-alone dispatch recomputes it from expert_idx);
+//   2. one wave per expert: exclusive scan of hist[e][*][*] in (choice, block)
+//      order -> offsets[e][c][b], expert_count[e] = min(total, C), and the empty
+//      tail of slot_token[e] set to -1;
+//   3. per token: rank among the earlier tokens of its block with the same
+//      expert for the same choice, slot = offset + rank (dropped if >= C), then
+//      the token's row is copied once from x into every expert slot it holds
+//      (16-byte vector loads/stores).
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// Phase 1 (stand-alone dispatch): one 256-thread block per 64-token block.
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ expert_idx,
+                                                            int T, int E, int k, int NB,
+                                                            int* __restrict__ hist) {
+  __shared__ int hl[kMaxK * kMaxE];
+  const int tid = threadIdx.x, b = blockIdx.x;
+  for (int i = tid; i < k * E; i += 256) hl[i] = 0;
+  __syncthreads();
+  const int t0 = b * 64;
+  const int n = min(64, T - t0) * k;
+  for (int i = tid; i < n; i += 256) {
+    const int e = expert_idx[static_cast<int64_t>(t0) * k + i];
+    const int c = i % k;
+    if (e >= 0 && e < E) atomicAdd(&hl[c * E + e], 1);
+  }
+  __syncthreads();
+  for (int i = tid; i < E * k; i += 256) {
+    const int e = i / k, c = i - e * k;
+    hist[(static_cast<int64_t>(e) * k + c) * NB + b] = hl[c * E + e];
+  }
+}
+
+// Phase 2: one wave per expert, four experts per block.
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int* __restrict__ hist, int E,
+                                                            int k, int NB, int64_t C,
+                                                            int* __restrict__ offsets,
+                                                            int32_t* __restrict__ expert_count,
+                                                            int32_t* __restrict__ slot_token) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int L = k * NB;
+  const int per = (L + kWave - 1) / kWave;
+  const int* seq = hist + static_cast<int64_t>(e) * L;
+  int* out = offsets + static_cast<int64_t>(e) * L;
+  const int j0 = lane * per;
+  const int j1 = min(L, j0 + per);
+  int sum = 0;
+  for (int j = j0; j < j1; ++j) sum += seq[j];
+  const int incl = wave_inclusive_scan(sum, lane);
+  int run = incl - sum;
+  for (int j = j0; j < j1; ++j) {
+    out[j] = run;
+    run += seq[j];
+  }
+  const int64_t total = __shfl(incl, kWave - 1, kWave);
+  const int64_t cnt = total < C ? total : C;
+  if (lane == 0) expert_count[e] = static_cast<int32_t>(cnt);
+  for (int64_t s = cnt + lane; s < C; s += kWave) slot_token[e * C + s] = -1;
+}
+
+// Phase 3: 16 tokens per 256-thread block (four blocks share one 64-token
+// router block); VEC = 16-byte vectors per row.
+constexpr int kSlotTokens = 16;
+
+__global__ __launch_bounds__(256) void dispatch_slot_gather_kernel(
+    const uint8_t* __restrict__ x, const int32_t* __restrict__ expert_idx, int T, int E, int k,
+    int NB, int64_t C, int64_t row_bytes, const int* __restrict__ offsets,
+    int32_t* __restrict__ slot, int32_t* __restrict__ slot_token, uint8_t* __restrict__ x_e) {
+  __shared__ int sidx[64 * kMaxK];
+  __shared__ int dst_e[kSlotTokens * kMaxK];
+  __shared__ int dst_s[kSlotTokens * kMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * kSlotTokens;
+  const int b = t0 / 64;
+  const int blk0 = b * 64;
+  const int tend = min(t0 + kSlotTokens, T);
+  // expert choices of the router block up to the end of this group
+  for (int i = tid; i < (tend - blk0) * k; i += 256)
+    sidx[i] = expert_idx[static_cast<int64_t>(blk0) * k + i];
+  __syncthreads();
+  if (tid < kSlotTokens * k) {
+    const int tl = tid / k, c = tid - tl * k;
+    const int t = t0 + tl;
+    int s = -1, e = -1;
+    if (t < T) {
+      e = sidx[(t - blk0) * k + c];
+      if (e >= 0 && e < E) {
+        int rank = 0;
+        for (int u = blk0; u < t; ++u) rank += sidx[(u - blk0) * k + c] == e;
+        const int64_t pos = static_cast<int64_t>(offsets[(static_cast<int64_t>(e) * k + c) * NB + b]) + rank;
+        if (pos < C) {
+          s = static_cast<int>(pos);
+          slot_token[e * C + pos] = t;
+        }
+      }
+      slot[static_cast<int64_t>(t) * k + c] = s;
+    }
+    dst_e[tl * k + c] = e;
+    dst_s[tl * k + c] = s;
+  }
+  __syncthreads();
+  const int64_t nvec = row_bytes / 16;
+  for (int tl = wave; tl < kSlotTokens; tl += 4) {
+    const int t = t0 + tl;
+    if (t >= T) break;
+    bool any = false;
+    for (int c = 0; c < k; ++c) any |= dst_s[tl * k + c] >= 0;
+    if (!any) continue;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(t) * row_bytes);
+    for (int64_t v = lane; v < nvec; v += kWave) {
+      const u32x4 val = src[v];
+      for (int c = 0; c < k; ++c) {
+        const int s = dst_s[tl * k + c];
+        if (s >= 0) {
+          const int e = dst_e[tl * k + c];
+          u32x4* dst = reinterpret_cast<u32x4*>(x_e + (e * C + s) * row_bytes);
+          dst[v] = val;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_dispatch_hist(const Plan& p, const int32_t* expert_idx, void* ws, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  int* hist = reinterpret_cast<int*>(ws_at(ws, p.off_hist));
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(p.NB), dim3(256), 0, s, expert_idx,
+                     static_cast<int>(p.T), p.E, p.k, p.NB, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scan(const Plan& p, int32_t* expert_count, int32_t* slot_token, void* ws,
+                                hipStream_t s) {
+  const int* hist = reinterpret_cast<const int*>(ws_at(ws, p.off_hist));
+  int* offsets = reinterpret_cast<int*>(ws_at(ws, p.off_offsets));
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3((p.E + 3) / 4), dim3(256), 0, s, hist, p.E, p.k,
+                     p.NB, p.C, offsets, expert_count, slot_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_slot_gather(const Plan& p, const void* x, const int32_t* expert_idx,
+                                       int32_t* slot, int32_t* slot_token, void* x_e, void* ws,
+                                       hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  const int* offsets = reinterpret_cast<const int*>(ws_at(ws, p.off_offsets));
+  const int nblk = static_cast<int>((p.T + kSlotTokens - 1) / kSlotTokens);
+  hipLaunchKernelGGL(dispatch_slot_gather_kernel, dim3(nblk), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(x), expert_idx, static_cast<int>(p.T), p.E, p.k,
+                     p.NB, p.C, p.d * p.elem, offsets, slot, slot_token,
+                     static_cast<uint8_t*>(x_e));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,51 @@
+// Host-side launch interface between the C ABI (moe_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kRouterBlock = 64;   // tokens per router block (histogram granularity)
+constexpr int kMaxE = 512;
+constexpr int kMaxK = 8;
+constexpr int kSplitBlocks = 64;   // blocks of the router-weight split kernel
+
+// Sizes derived once from a validated configuration.
+struct Plan {
+  int64_t T, d, f, C;
+  int E, k, Epad, NB;      // Epad: E rounded up to 32; NB: router blocks of 64 tokens
+  int dtype, act, route, n_groups;
+  uint64_t rre_seed;
+  int elem;                // bytes per element of dtype
+  // workspace byte offsets
+  int64_t off_region[8];
+  int64_t off_hist, off_offsets, off_planes, off_flags, total;
+};
+
+// router.hip
+hipError_t launch_router_split(const Plan& p, const float* w_r, void* ws, hipStream_t s);
+hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, const float* bias,
+                              int32_t* expert_idx, float* gate, void* ws, hipStream_t s);
+hipError_t launch_router_rre(const Plan& p, const int32_t* group_id, int32_t* expert_idx,
+                             float* gate, void* ws, hipStream_t s);
+
+// dispatch.hip
+hipError_t launch_dispatch_hist(const Plan& p, const int32_t* expert_idx, void* ws, hipStream_t s);
+hipError_t launch_dispatch_scan(const Plan& p, int32_t* expert_count, int32_t* slot_token, void* ws,
+                                hipStream_t s);
+hipError_t launch_dispatch_slot_gather(const Plan& p, const void* x, const int32_t* expert_idx,
+                                       int32_t* slot, int32_t* slot_token, void* x_e, void* ws,
+                                       hipStream_t s);
+
+// expert_ffn.hip
+hipError_t launch_expert_ffn(const Plan& p, const void* x_e, const int32_t* expert_count,
+                             const void* w1, const void* w2, void* y_e, void* ws, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const Plan& p, const void* y_e, const int32_t* expert_idx,
+                          const int32_t* slot, const float* gate, void* y, hipStream_t s);
+
+inline char* ws_at(void* ws, int64_t off) { return static_cast<char*>(ws) + off; }
+
+}  // namespace moe

@@ -1,0 +1,434 @@
+// Router kernels: fused logits + softmax + top-k (+ per-block expert histogram),
+// and the weightless random-routed-experts pick.
+//
+// Method (Switch Transformers notes, section 2.1): logits h(x) = W_r . x over the
+// N experts, gate p_i = exp(h_i) / sum_j exp(h_j) (Eq. 1), the token goes to the
+// top-k experts.  Section 2.4 keeps the router arithmetic in float32.  X-MoE
+// top-1/top-2 routing (TorchScale review).  Random Routed Experts (PanGu-Sigma
+// review): a uniform pick inside the token's expert group, no learned gate.
+//
+// gfx950 design.  A work-group owns 64 tokens.  The logits tile [64 x E] is a
+// skinny GEMM done on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with float32
+// accumulation: x is bf16 already, and the float32 router weight is split once
+// per call into three bf16 planes hi + mid + lo that sum to it exactly, so every
+// product is exact; when the weight is bf16-exact (mid = lo = 0, detected on the
+// device) only the hi plane is used.  Token and weight tiles are staged in LDS
+// (double-buffered); the logits tile then goes to LDS and each wave ranks whole
+// tokens with 64-bit keys (logit, then lower index) reduced across the wave.
+// The expert histogram of the block is built in LDS for the dispatch scan.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+#include <math.h>
+
+namespace moe {
+
+// ---- total order on (logit desc, expert asc) as one unsigned 64-bit key ----
+__device__ __forceinline__ uint32_t ordered_bits(float h) {
+  uint32_t u = __float_as_uint(h);
+  if (h == 0.0f) u = 0u;  // -0 ranks equal to +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  uint32_t o = static_cast<uint32_t>(key >> 32);
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t make_key(float h, int e) {
+  return (static_cast<uint64_t>(ordered_bits(h)) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - e);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+
+// Rank the tokens of one block.  lg: logits [64][ld] in LDS (bias not yet added).
+// Wave w handles tokens w, w+4, ...; lane l holds experts l, l+64, ...
+__device__ void topk_epilogue(const float* lg, int ld, int tok0, int ntok, int E, int k,
+                              const float* __restrict__ bias, int32_t* __restrict__ expert_idx,
+                              float* __restrict__ gate, int* hl, int ldh, int wave, int lane) {
+  const int nper = (E + kWave - 1) / kWave;  // <= 8
+  for (int t = wave; t < ntok; t += 4) {
+    const float* row = lg + t * ld;
+    float hv[kMaxE / kWave];
+    uint64_t kv[kMaxE / kWave];
+#pragma unroll
+    for (int i = 0; i < kMaxE / kWave; ++i) {
+      hv[i] = -INFINITY;
+      kv[i] = 0;
+      const int e = lane + kWave * i;
+      if (i < nper && e < E) {
+        float h = row[e];
+        if (bias) h = h + bias[e];  // one float32 rounding after the full dot product
+        hv[i] = h;
+        kv[i] = make_key(h, e);
+      }
+    }
+    uint64_t best0 = 0, bestc = 0;
+    for (int c = 0; c < k; ++c) {
+      uint64_t m = 0;
+#pragma unroll
+      for (int i = 0; i < kMaxE / kWave; ++i) m = kv[i] > m ? kv[i] : m;
+      m = wave_max_u64(m);
+#pragma unroll
+      for (int i = 0; i < kMaxE / kWave; ++i)
+        if (kv[i] == m) kv[i] = 0;  // keys are unique: removes exactly the winner
+      if (c == 0) best0 = m;
+      if (lane == c) bestc = m;
+    }
+    const float hmax = key_logit(best0);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxE / kWave; ++i) s += expf(hv[i] - hmax);  // exp(-inf) = 0
+    s = wave_sum(s);
+    if (lane < k) {
+      const int e = key_expert(bestc);
+      const float p = expf(key_logit(bestc) - hmax) / s;
+      const int64_t o = static_cast<int64_t>(tok0 + t) * k + lane;
+      expert_idx[o] = e;
+      gate[o] = p;
+      atomicAdd(&hl[lane * ldh + e], 1);
+    }
+  }
+}
+
+__device__ __forceinline__ void write_hist(const int* hl, int ldh, int E, int k, int NB, int b,
+                                           int* __restrict__ hist, int tid, int nthreads) {
+  for (int i = tid; i < E * k; i += nthreads) {
+    const int e = i / k, c = i - e * k;
+    hist[(static_cast<int64_t>(e) * k + c) * NB + b] = hl[c * ldh + e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split the float32 router weight into bf16 planes hi, mid, lo with
+// w = hi + mid + lo exactly (each step rounds the remainder to nearest bf16;
+// the remainders are exact in float32).  Rows E..Epad-1 are zero.  Block b
+// writes flags[b] = 1 if any mid/lo element of its share is non-zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ w_r, int E,
+                                                           int Epad, int d,
+                                                           bf16_t* __restrict__ planes,
+                                                           int* __restrict__ flags) {
+  const int64_t n = static_cast<int64_t>(Epad) * d;
+  const int64_t lim = static_cast<int64_t>(E) * d;
+  int nz = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const float w = i < lim ? w_r[i] : 0.f;
+    const bf16_t hi = f32_to_bf16(w);
+    const float r1 = w - bf16_to_f32(hi);
+    const bf16_t mid = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(mid);
+    const bf16_t lo = f32_to_bf16(r2);
+    planes[i] = hi;
+    planes[n + i] = mid;
+    planes[2 * n + i] = lo;
+    nz |= ((mid & 0x7FFF) | (lo & 0x7FFF)) != 0;
+  }
+  nz = __syncthreads_or(nz);
+  if (threadIdx.x == 0) flags[blockIdx.x] = nz;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 router: MFMA logits tile + top-k epilogue.
+// ---------------------------------------------------------------------------
+constexpr int RBK = 32;        // k elements per LDS stage
+constexpr int RLD = RBK + 8;   // padded LDS row, bf16 elements (80 bytes: conflict-free frags)
+
+__host__ __device__ inline int64_t router_bf16_stage_bytes(int Epad) {
+  return 2LL * (64 + Epad) * RLD * 2;
+}
+__host__ __device__ inline int64_t router_lg_bytes(int Epad) { return 64LL * (Epad + 4) * 4; }
+
+// MAXU: expert tiles of 32 per wave (wave w owns tiles w, w+4, ...); Epad <= 128 * MAXU.
+template <int MAXU>
+__global__ __launch_bounds__(256) void router_bf16_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, const int* __restrict__ flags,
+    const float* __restrict__ bias, int T, int d, int E, int Epad, int k,
+    int32_t* __restrict__ expert_idx, float* __restrict__ gate, int* __restrict__ hist, int NB) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  const int tok0 = b * 64;
+  const int ntok = min(64, T - tok0);
+  const int n_et = Epad / 32;
+
+  bf16_t* sx = reinterpret_cast<bf16_t*>(smem);   // [2][64][RLD]
+  bf16_t* sw = sx + 2 * 64 * RLD;                 // [2][Epad][RLD]
+  float* lg = reinterpret_cast<float*>(smem);     // [64][Epad + 4], after the K loop
+  const int64_t body = max(router_bf16_stage_bytes(Epad), router_lg_bytes(Epad));
+  int* hl = reinterpret_cast<int*>(smem + body);  // [k][Epad]
+
+  for (int i = tid; i < k * Epad; i += 256) hl[i] = 0;
+
+  int any = 0;
+  for (int i = 0; i < kSplitBlocks; ++i) any |= flags[i];
+  const int nplanes = any ? 3 : 1;
+  const int KT = d / RBK;
+  const int nsteps = nplanes * KT;
+  const int64_t plane_elems = static_cast<int64_t>(Epad) * d;
+
+  floatx16 acc[MAXU][2];
+#pragma unroll
+  for (int u = 0; u < MAXU; ++u)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[u][tt][r] = 0.f;
+
+  u32x4 rx;
+  u32x4 rw[2 * MAXU];
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const int xr = tid >> 2, xc = tid & 3;
+  const int tx = tok0 + xr;
+
+  auto gload = [&](int step) {
+    const int p = step / KT;
+    const int k0 = (step - p * KT) * RBK;
+    rx = tx < T ? *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(tx) * d + k0 + xc * 8)
+                : zero4;
+    const bf16_t* wp = planes + p * plane_elems;
+#pragma unroll
+    for (int i = 0; i < 2 * MAXU; ++i) {
+      const int id = tid + 256 * i;
+      if (id < Epad * 4) {
+        const int row = id >> 2, c = id & 3;
+        rw[i] = *reinterpret_cast<const u32x4*>(wp + static_cast<int64_t>(row) * d + k0 + c * 8);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+    *reinterpret_cast<u32x4*>(sx + (buf * 64 + xr) * RLD + xc * 8) = rx;
+#pragma unroll
+    for (int i = 0; i < 2 * MAXU; ++i) {
+      const int id = tid + 256 * i;
+      if (id < Epad * 4) {
+        const int row = id >> 2, c = id & 3;
+        *reinterpret_cast<u32x4*>(sw + (buf * Epad + row) * RLD + c * 8) = rw[i];
+      }
+    }
+  };
+
+  const int fr = lane & 31;         // fragment row (expert or token within the tile)
+  const int fk = (lane >> 5) * 8;   // fragment k offset
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int step = 0; step < nsteps; ++step) {
+    const int buf = step & 1;
+    if (step + 1 < nsteps) gload(step + 1);
+#pragma unroll
+    for (int k16 = 0; k16 < RBK / 16; ++k16) {
+      const bf16x8 bq0 = *reinterpret_cast<const bf16x8*>(sx + (buf * 64 + fr) * RLD + k16 * 16 + fk);
+      const bf16x8 bq1 = *reinterpret_cast<const bf16x8*>(sx + (buf * 64 + 32 + fr) * RLD + k16 * 16 + fk);
+#pragma unroll
+      for (int u = 0; u < MAXU; ++u) {
+        const int et = wave + 4 * u;
+        if (et < n_et) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sw + (buf * Epad + et * 32 + fr) * RLD + k16 * 16 + fk);
+          acc[u][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq0, acc[u][0], 0, 0, 0);
+          acc[u][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq1, acc[u][1], 0, 0, 0);
+        }
+      }
+    }
+    if (step + 1 < nsteps) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // D[i][j] of a 32x32 tile: lane holds column j = lane % 32 (token) and rows
+  // i = 8*(r/4) + 4*(lane/32) + r%4 (experts) of accumulator element r.
+  const int ld = Epad + 4;
+#pragma unroll
+  for (int u = 0; u < MAXU; ++u) {
+    const int et = wave + 4 * u;
+    if (et < n_et) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int t = tt * 32 + fr;
+          const int e = et * 32 + 8 * g + 4 * (lane >> 5);
+          floatx4 v = {acc[u][tt][4 * g], acc[u][tt][4 * g + 1], acc[u][tt][4 * g + 2],
+                       acc[u][tt][4 * g + 3]};
+          *reinterpret_cast<floatx4*>(lg + t * ld + e) = v;
+        }
+    }
+  }
+  __syncthreads();
+  topk_epilogue(lg, ld, tok0, ntok, E, k, bias, expert_idx, gate, hl, Epad, wave, lane);
+  __syncthreads();
+  write_hist(hl, Epad, E, k, NB, b, hist, tid, 256);
+}
+
+// ---------------------------------------------------------------------------
+// float32 router (float32 token dtype): float32 FMA dot products.
+// NACC = experts per thread; the block covers Ecap = 4 * NACC >= E experts.
+// ---------------------------------------------------------------------------
+constexpr int FBK = 32;
+__host__ __device__ inline int64_t router_f32_stage_bytes(int Ecap) {
+  return (64LL + Ecap) * (FBK + 1) * 4;
+}
+
+template <int NACC>
+__global__ __launch_bounds__(256) void router_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ bias,
+    int T, int d, int E, int k, int32_t* __restrict__ expert_idx, float* __restrict__ gate,
+    int* __restrict__ hist, int NB) {
+  constexpr int Ecap = 4 * NACC;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  const int tok0 = b * 64;
+  const int ntok = min(64, T - tok0);
+  float* sx = reinterpret_cast<float*>(smem);  // [64][FBK+1]
+  float* sw = sx + 64 * (FBK + 1);             // [Ecap][FBK+1]
+  float* lg = reinterpret_cast<float*>(smem);  // [64][Ecap + 4]
+  const int64_t body = max(router_f32_stage_bytes(Ecap), router_lg_bytes(Ecap));
+  int* hl = reinterpret_cast<int*>(smem + body);
+
+  for (int i = tid; i < k * Ecap; i += 256) hl[i] = 0;
+
+  float acc[NACC];
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) acc[j] = 0.f;
+  const int t = tid & 63, eg = tid >> 6;
+  for (int k0 = 0; k0 < d; k0 += FBK) {
+    for (int id = tid; id < 64 * FBK; id += 256) {
+      const int r = id / FBK, c = id - r * FBK;
+      sx[r * (FBK + 1) + c] = tok0 + r < T ? x[static_cast<int64_t>(tok0 + r) * d + k0 + c] : 0.f;
+    }
+    for (int id = tid; id < Ecap * FBK; id += 256) {
+      const int r = id / FBK, c = id - r * FBK;
+      sw[r * (FBK + 1) + c] = r < E ? w_r[static_cast<int64_t>(r) * d + k0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < FBK; ++kk) {
+      const float xv = sx[t * (FBK + 1) + kk];
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) acc[j] = fmaf(xv, sw[(eg + 4 * j) * (FBK + 1) + kk], acc[j]);
+    }
+    __syncthreads();
+  }
+  const int ld = Ecap + 4;
+#pragma unroll
+  for (int j = 0; j < NACC; ++j) lg[t * ld + eg + 4 * j] = acc[j];
+  __syncthreads();
+  topk_epilogue(lg, ld, tok0, ntok, E, k, bias, expert_idx, gate, hl, Ecap, wave, lane);
+  __syncthreads();
+  write_hist(hl, Ecap, E, k, NB, b, hist, tid, 256);
+}
+
+// ---------------------------------------------------------------------------
+// Random Routed Experts: expert = g * size + (SplitMix64 output t) mod size.
+// SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): output t of seed s mixes the
+// state s + (t+1) * 0x9E3779B97F4A7C15 with two xor-shift-multiply rounds.
+// One block of 64 threads per router block of 64 tokens.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t t) {
+  uint64_t z = seed + (t + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ __launch_bounds__(64) void router_rre_kernel(const int32_t* __restrict__ group_id, int T,
+                                                        int E, int n_groups, uint64_t seed,
+                                                        int32_t* __restrict__ expert_idx,
+                                                        float* __restrict__ gate,
+                                                        int* __restrict__ hist, int NB) {
+  __shared__ int hl[kMaxE];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  for (int i = tid; i < E; i += 64) hl[i] = 0;
+  __syncthreads();
+  const int t = b * 64 + tid;
+  if (t < T) {
+    const int g = group_id[t];
+    const int size = E / n_groups;
+    int e = -1;
+    if (g >= 0 && g < n_groups) {
+      e = g * size + static_cast<int>(splitmix64_at(seed, static_cast<uint64_t>(t)) %
+                                      static_cast<uint64_t>(size));
+      atomicAdd(&hl[e], 1);
+    }
+    expert_idx[t] = e;
+    gate[t] = e >= 0 ? 1.0f : 0.0f;
+  }
+  __syncthreads();
+  write_hist(hl, kMaxE, E, 1, NB, b, hist, tid, 64);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_router_split(const Plan& p, const float* w_r, void* ws, hipStream_t s) {
+  bf16_t* planes = reinterpret_cast<bf16_t*>(ws_at(ws, p.off_planes));
+  int* flags = reinterpret_cast<int*>(ws_at(ws, p.off_flags));
+  hipLaunchKernelGGL(router_split_kernel, dim3(kSplitBlocks), dim3(256), 0, s, w_r, p.E, p.Epad,
+                     static_cast<int>(p.d), planes, flags);
+  return hipGetLastError();
+}
+
+template <typename K>
+static hipError_t set_lds(K kernel, int64_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, const float* bias,
+                              int32_t* expert_idx, float* gate, void* ws, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  int* hist = reinterpret_cast<int*>(ws_at(ws, p.off_hist));
+  const int T = static_cast<int>(p.T), d = static_cast<int>(p.d);
+  hipError_t err;
+  if (p.dtype == 1) {
+    err = launch_router_split(p, w_r, ws, s);
+    if (err != hipSuccess) return err;
+    const bf16_t* planes = reinterpret_cast<const bf16_t*>(ws_at(ws, p.off_planes));
+    const int* flags = reinterpret_cast<const int*>(ws_at(ws, p.off_flags));
+    const int64_t lds = std::max(router_bf16_stage_bytes(p.Epad), router_lg_bytes(p.Epad)) +
+                        4LL * p.k * p.Epad;
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+#define MOE_ROUTER_BF16(U)                                                                    \
+  do {                                                                                        \
+    if ((err = set_lds(router_bf16_kernel<U>, lds)) != hipSuccess) return err;                \
+    hipLaunchKernelGGL(router_bf16_kernel<U>, dim3(p.NB), dim3(256), lds, s, xb, planes, flags, \
+                       bias, T, d, p.E, p.Epad, p.k, expert_idx, gate, hist, p.NB);           \
+  } while (0)
+    if (p.Epad <= 128) MOE_ROUTER_BF16(1);
+    else if (p.Epad <= 256) MOE_ROUTER_BF16(2);
+    else MOE_ROUTER_BF16(4);
+#undef MOE_ROUTER_BF16
+  } else {
+    const float* xf = static_cast<const float*>(x);
+#define MOE_ROUTER_F32(N)                                                                        \
+  do {                                                                                           \
+    const int64_t lds = std::max(router_f32_stage_bytes(4 * N), router_lg_bytes(4 * N)) +        \
+                        4LL * p.k * 4 * N;                                                       \
+    if ((err = set_lds(router_f32_kernel<N>, lds)) != hipSuccess) return err;                    \
+    hipLaunchKernelGGL(router_f32_kernel<N>, dim3(p.NB), dim3(256), lds, s, xf, w_r, bias, T, d, \
+                       p.E, p.k, expert_idx, gate, hist, p.NB);                                  \
+  } while (0)
+    if (p.E <= 32) MOE_ROUTER_F32(8);
+    else if (p.E <= 64) MOE_ROUTER_F32(16);
+    else if (p.E <= 128) MOE_ROUTER_F32(32);
+    else if (p.E <= 256) MOE_ROUTER_F32(64);
+    else MOE_ROUTER_F32(128);
+#undef MOE_ROUTER_F32
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_rre(const Plan& p, const int32_t* group_id, int32_t* expert_idx,
+                             float* gate, void* ws, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  int* hist = reinterpret_cast<int*>(ws_at(ws, p.off_hist));
+  hipLaunchKernelGGL(router_rre_kernel, dim3(p.NB), dim3(64), 0, s, group_id,
+                     static_cast<int>(p.T), p.E, p.n_groups, p.rre_seed, expert_idx, gate, hist,
+                     p.NB);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Routing, slots, counts, slot maps and gathered rows must match bit for bit;
+gates within ``gate_tol``; expert and layer outputs within the normwise
+max-abs-rel tolerance (2e-2 bf16 with float32 accumulation, 1e-5 float32).
+Inputs are the seeded workloads of moe_workloads at sizes the oracle finishes
+in seconds (several router blocks, several GEMM tiles, ragged tails).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as W
+import oracle
+from gpu_util import (Dev, check_layer_output, check_routing, max_abs_rel, out_tol, raw_bits,
+                      to_dev, to_host_f64)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = sorted(W.TEST_WORKLOADS)
+
+
+def _oracle(wl, inputs):
+    return oracle.forward(wl, inputs)
+
+
+def _served(ref):
+    return (ref["slot"] >= 0).any(axis=1)
+
+
+def _check_x_e(wl, got_x_e, ref, inputs):
+    xe = raw_bits(got_x_e)
+    x = inputs["x"]
+    for e in range(wl.E):
+        n = int(ref["expert_count"][e])
+        np.testing.assert_array_equal(xe[e, :n], x[ref["slot_token"][e, :n]], err_msg=f"x_e expert {e}")
+
+
+def _check_y_e(wl, got_y_e, ref):
+    ye = to_host_f64(got_y_e)
+    for e in range(wl.E):
+        n = int(ref["expert_count"][e])
+        if n:
+            err = max_abs_rel(ye[e, :n], ref["y_e"][e])
+            assert err <= out_tol(wl), f"y_e expert {e}: {err:.3g}"
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_steps_match_oracle(name):
+    wl = W.TEST_WORKLOADS[name]
+    print(f"[gpu] steps {name}", flush=True)
+    inputs = W.make_inputs(wl)
+    ref = _oracle(wl, inputs)
+    dev = Dev(wl, inputs)
+    got = dev.run_steps()
+    check_routing(wl, got, ref, name)
+    _check_x_e(wl, got["x_e"], ref, inputs)
+    _check_y_e(wl, got["y_e"], ref)
+    check_layer_output(wl, to_host_f64(got["y"]), ref["y"], _served(ref), name)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_forward_matches_oracle_and_steps(name):
+    wl = W.TEST_WORKLOADS[name]
+    print(f"[gpu] forward {name}", flush=True)
+    inputs = W.make_inputs(wl)
+    ref = _oracle(wl, inputs)
+    dev = Dev(wl, inputs)
+    fw = dev.run_forward()
+    check_routing(wl, fw, ref, name)
+    check_layer_output(wl, to_host_f64(fw["y"]), ref["y"], _served(ref), name)
+    steps = dev.run_steps()
+    assert torch.equal(fw["y"], steps["y"]), "forward and step-wise results differ"
+
+
+@pytest.mark.parametrize("name", ["switch_small_bf16", "xmoe_small_bf16", "tiny_switch_f32"])
+def test_combine_alone(name):
+    """Combine on oracle-provided expert outputs (rounded to the storage dtype)."""
+    wl = W.TEST_WORKLOADS[name]
+    inputs = W.make_inputs(wl)
+    ref = _oracle(wl, inputs)
+    dev = Dev(wl, inputs)
+    C = ref["capacity"]
+    ye = np.zeros((wl.E, C, wl.d_model))
+    for e in range(wl.E):
+        ye[e, :len(ref["y_e"][e])] = ref["y_e"][e]
+    if wl.dtype == "bf16":
+        ye_store = W.f32_to_bf16_bits(ye.astype(np.float32))
+        ye_val = W.bf16_bits_to_f32(ye_store).astype(np.float64)
+    else:
+        ye_store = ye.astype(np.float32)
+        ye_val = ye_store.astype(np.float64)
+    y_ref = oracle.combine([ye_val[e] for e in range(wl.E)], ref["expert_idx"], ref["slot"],
+                           ref["gate"], wl.d_model)
+    y = torch.empty((wl.T, wl.d_model), dtype=dev.x.dtype, device="cuda")
+    import sparse_mixture_experts_13_amd as moe
+    moe.combine(dev.cfg, to_dev(ye_store), to_dev(ref["expert_idx"]), to_dev(ref["slot"]),
+                to_dev(ref["gate"]), y)
+    torch.cuda.synchronize()
+    tol = 2.0 ** -8 if wl.dtype == "bf16" else 1e-6   # one output rounding
+    err = max_abs_rel(to_host_f64(y), y_ref)
+    assert err <= tol, err
+    assert (to_host_f64(y)[~_served(ref)] == 0).all()
+
+
+def test_repeated_runs_bit_identical():
+    wl = W.TEST_WORKLOADS["zipf_small_bf16"]
+    dev = Dev(wl, W.make_inputs(wl))
+    first = dev.run_forward()
+    y0 = first["y"].clone()
+    idx0 = first["expert_idx"].clone()
+    slot0 = first["slot"].clone()
+    for _ in range(9):
+        again = dev.run_forward()
+        assert torch.equal(again["y"], y0)
+        assert torch.equal(again["expert_idx"], idx0)
+        assert torch.equal(again["slot"], slot0)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+def _run_case(wl, inputs, label):
+    print(f"[gpu] case {label}", flush=True)
+    ref = _oracle(wl, inputs)
+    dev = Dev(wl, inputs)
+    got = dev.run_steps()
+    check_routing(wl, got, ref, label)
+    if wl.T:
+        _check_x_e(wl, got["x_e"], ref, inputs)
+        check_layer_output(wl, to_host_f64(got["y"]), ref["y"], _served(ref), label)
+    fw = dev.run_forward()
+    check_routing(wl, fw, ref, label + " forward")
+    if wl.T:
+        check_layer_output(wl, to_host_f64(fw["y"]), ref["y"], _served(ref), label + " forward")
+    return ref, got
+
+
+BASE = W.Workload("edge", T=300, d_model=128, d_ff=192, E=10, k=2, capacity_factor=1.0,
+                  act="gelu", dtype="bf16")
+
+
+def test_single_token():
+    wl = BASE.replace(T=1)
+    _run_case(wl, W.make_inputs(wl), "T=1")
+
+
+def test_empty_input():
+    wl = BASE.replace(T=0)
+    inputs = W.make_inputs(wl)
+    ref = _oracle(wl, inputs)
+    dev = Dev(wl, inputs)
+    got = dev.run_steps()
+    assert got["expert_count"].cpu().numpy().tolist() == [0] * wl.E
+    fw = dev.run_forward()
+    assert fw["y"].numel() == 0 and ref["capacity"] == 0
+
+
+def test_capacity_one():
+    wl = BASE.replace(T=40, E=8, k=1, capacity_factor=0.15)
+    inputs = W.make_inputs(wl)
+    assert oracle.capacity(wl.T, wl.E, wl.k, wl.capacity_factor) == 1
+    ref, _ = _run_case(wl, inputs, "C=1")
+    assert (ref["expert_count"] <= 1).all()
+
+
+def test_one_expert_takes_all():
+    wl = BASE.replace(T=500, E=16, k=2, capacity_factor=1.25)
+    inputs = W.make_inputs(wl)
+    inputs["bias"] = np.zeros(wl.E, np.float32)
+    inputs["bias"][3] = 1000.0     # expert 3 first for every token: most first choices drop
+    inputs["bias"][9] = 500.0      # expert 9 second for every token
+    ref, _ = _run_case(wl, inputs, "skew")
+    assert ref["expert_count"][3] == ref["capacity"]
+    assert (ref["slot"][:, 0] < 0).sum() == wl.T - ref["capacity"]
+
+
+def test_all_logits_tie():
+    wl = BASE.replace(T=200, E=12, k=2, capacity_factor=4.0)
+    inputs = W.make_inputs(wl)
+    inputs["w_r"] = np.zeros_like(inputs["w_r"])     # every logit is 0: ties to experts 0, 1
+    ref, _ = _run_case(wl, inputs, "ties")
+    assert (ref["expert_idx"] == [0, 1]).all()
+
+
+def test_signed_zero_logits():
+    wl = BASE.replace(T=128, E=8, k=2, capacity_factor=2.0)
+    inputs = W.make_inputs(wl)
+    x = W.bf16_bits_to_f32(inputs["x"])
+    x[::3] = 0.0                                     # zero rows: logits are +0 or -0
+    inputs["x"] = W.f32_to_bf16_bits(x)
+    inputs["w_r"][::2] = -np.abs(inputs["w_r"][::2])  # negative rows give -0.0 products
+    ref, _ = _run_case(wl, inputs, "signed zeros")
+    assert (ref["expert_idx"][::3] == [0, 1]).all()
+
+
+def test_second_third_choice_tie():
+    wl = BASE.replace(T=256, E=6, k=2, capacity_factor=2.0)
+    inputs = W.make_inputs(wl)
+    inputs["w_r"][4] = inputs["w_r"][2]              # experts 2 and 4 always tie
+    inputs["w_r"][5] = inputs["w_r"][1]              # experts 1 and 5 always tie
+    _run_case(wl, inputs, "2nd/3rd ties")
+
+
+def test_non_dyadic_router_weight():
+    """Gaussian float32 router weight: exercises the three-plane bf16 split.
+
+    Logits are then not exact in float32, so a token whose k-th and (k+1)-th
+    logits are closer than the float32 error bound may legitimately rank either
+    way; the check compares routing on every token with a clear margin and
+    verifies the rest is a valid choice.
+    """
+    wl = BASE.replace(T=400, E=24, k=2, capacity_factor=8.0, w_r_dist="gauss")
+    inputs = W.make_inputs(wl)
+    ref = _oracle(wl, inputs)
+    dev = Dev(wl, inputs)
+    got = dev.run_steps()
+    idx = got["expert_idx"].cpu().numpy()
+    h = ref["logits"].astype(np.float64)
+    srt = -np.sort(-h, axis=1)
+    margin = np.minimum(srt[:, 0] - srt[:, 1], srt[:, 1] - srt[:, 2])
+    bound = 1e-5 * np.abs(h).max()
+    clear = margin > bound
+    assert clear.mean() > 0.9
+    np.testing.assert_array_equal(idx[clear], ref["expert_idx"][clear])
+    for t in np.nonzero(~clear)[0]:
+        chosen = h[t, idx[t]]
+        assert np.all(np.abs(np.sort(chosen)[::-1] - srt[t, :2]) <= bound)
+    # capacity is large: everything is served, so y compares on clear tokens
+    y = to_host_f64(got["y"])
+    err = max_abs_rel(y[clear], ref["y"][clear])
+    assert err <= out_tol(wl), err
+
+
+def test_max_experts_and_choices():
+    wl = BASE.replace(T=200, d_model=64, d_ff=64, E=512, k=8, capacity_factor=16.0, act="relu")
+    _run_case(wl, W.make_inputs(wl), "E=512 k=8")
+
+
+def test_single_expert():
+    wl = BASE.replace(T=130, E=1, k=1, capacity_factor=1.0)
+    ref, _ = _run_case(wl, W.make_inputs(wl), "E=1")
+    assert (ref["gate"] == 1.0).all()
+
+
+def test_f32_gelu_top2():
+    wl = BASE.replace(T=333, d_model=64, d_ff=128, E=9, k=2, capacity_factor=1.1, dtype="f32")
+    _run_case(wl, W.make_inputs(wl), "f32 top-2 gelu")
+
+
+def test_rre_invalid_group_ids():
+    wl = W.TEST_WORKLOADS["rre_small_bf16"].replace(T=200)
+    inputs = W.make_inputs(wl)
+    inputs["group_id"][::7] = 9      # out of range: routed nowhere
+    inputs["group_id"][1::7] = -1
+    ref, got = _run_case(wl, inputs, "rre bad groups")
+    assert (got["expert_idx"].cpu().numpy()[::7] == -1).all()
