@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""MoE-layer forward throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one moe_forward call (router -> dispatch -> gather -> expert FFN ->
+combine) over the whole synthetic batch, inputs already resident in HBM.
+Prints ONE JSON line: tokens/s, the roofline of the dominant kernel (timed
+live with HIP events on the stream it runs on), and the CPU oracle timed on
+the host cores as a baseline.
+
+The default workload is the Switch-Base-shaped layer: T = 8192 tokens
+(8 sequences x 1024), d_model 768, d_ff 3072, 128 experts, top-1,
+capacity factor 1.0, ReLU, bf16 with float32 accumulation.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+FP32_PEAK_TFLOPS = 157.3
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "sparse_mixture_experts_13_amd", "csrc", "expert_ffn.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="switch_base_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=25.0,
+                    help="bound on the oracle's CPU time for the baseline sample")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain copy of known size (counter calibration runs)")
+    return ap.parse_args()
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it is current."""
+    path = os.path.join(PROFILES, "pmc_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    sha = source_sha(KERNEL_SRC)
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        kv = dict(item.split("=", 1) for item in line.split())
+        if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("source_sha") == sha:
+            return float(kv["hbm_bytes_per_launch"])
+    return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "expert-parallel path is a design, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_workloads as W
+    import sparse_mixture_experts_13_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = W.get(args.workload)
+    cfg = moe.config_for(wl)
+    C = moe.capacity(cfg)
+    dev = "cuda"
+    elem = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    es = 2 if wl.dtype == "bf16" else 4
+
+    # ---- inputs (seeded, synthetic), resident in HBM ----
+    t_gen = time.time()
+    inputs = W.make_inputs(wl, with_weights=False)
+
+    def up(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x, w_r, bias, gid = up(inputs["x"]), up(inputs["w_r"]), up(inputs["bias"]), up(inputs["group_id"])
+    w1 = torch.empty((wl.E, wl.d_ff, wl.d_model), dtype=elem, device=dev)
+    w2 = torch.empty((wl.E, wl.d_model, wl.d_ff), dtype=elem, device=dev)
+    keep_host = not args.no_cpu_baseline
+    host_w1 = np.empty((wl.E, wl.d_ff, wl.d_model), np.uint16 if es == 2 else np.float32) if keep_host else None
+    host_w2 = np.empty((wl.E, wl.d_model, wl.d_ff), np.uint16 if es == 2 else np.float32) if keep_host else None
+
+    def put(e, a, b):
+        w1[e].copy_(up(a))
+        w2[e].copy_(up(b))
+        if keep_host:
+            host_w1[e] = a
+            host_w2[e] = b
+
+    W.for_each_expert(wl, put, threads=8)
+    y = torch.empty((wl.T, wl.d_model), dtype=elem, device=dev)
+    ws = moe.alloc_workspace(cfg)
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.forward(cfg, x, w_r, bias, gid, w1, w2, y, ws, stream)
+
+    # ---- whole-layer throughput ----
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall_ms / args.steps
+    tokens_per_s = wl.T / (ms_per_step / 1e3)
+
+    counts = moe.workspace_view(ws, cfg, "expert_count").cpu().numpy().astype(np.int64)
+    served = int(counts.sum())
+    active = int((counts > 0).sum())
+    drops = wl.T * wl.k - served
+
+    # ---- per-kernel durations, live, with HIP events on the launch stream ----
+    x_e = moe.workspace_view(ws, cfg, "x_e")
+    hidden = moe.workspace_view(ws, cfg, "hidden")
+    y_e = moe.workspace_view(ws, cfg, "y_e")
+    cnt_t = moe.workspace_view(ws, cfg, "expert_count")
+    idx_t = moe.workspace_view(ws, cfg, "expert_idx")
+    gate_t = moe.workspace_view(ws, cfg, "gate")
+    slot_t = moe.workspace_view(ws, cfg, "slot")
+    st_t = moe.workspace_view(ws, cfg, "slot_token")
+    idx2 = torch.empty_like(idx_t)
+    gate2 = torch.empty_like(gate_t)
+    slot2 = torch.empty_like(slot_t)
+    cnt2 = torch.empty_like(cnt_t)
+    st2 = torch.empty_like(st_t)
+    xe2 = torch.empty_like(x_e)
+    y2 = torch.empty_like(y)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps   # microseconds per call
+
+    R = args.kernel_reps
+    kern_us = {
+        "router": timed(lambda: moe.router(cfg, x, w_r, bias, gid, idx2, gate2, ws, stream), R),
+        "dispatch": timed(lambda: moe.dispatch(cfg, x, idx_t, slot2, cnt2, st2, xe2, ws, stream), R),
+        "gemm_up": timed(lambda: moe.expert_up(cfg, x_e, cnt_t, w1, hidden, stream), R),
+        "gemm_down": timed(lambda: moe.expert_down(cfg, hidden, cnt_t, w2, y_e, stream), R),
+        "combine": timed(lambda: moe.combine(cfg, y_e, idx_t, slot_t, gate_t, y2, stream), R),
+    }
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        kern_us["copy_256MiB"] = timed(lambda: dst.copy_(src), R)
+
+    # algorithmic bytes / flops per launch (served rows only; weights of experts with tokens)
+    d, f = wl.d_model, wl.d_ff
+    wbytes = active * d * f * es
+    algo = {
+        "gemm_up": dict(bytes=wbytes + served * d * es + served * f * es, flops=2.0 * served * d * f),
+        "gemm_down": dict(bytes=wbytes + served * f * es + served * d * es, flops=2.0 * served * d * f),
+        "router": dict(bytes=wl.T * d * es + (wl.E * d * 4 if wl.route == "topk" else wl.T * 4)
+                       + 8 * wl.T * wl.k, flops=2.0 * wl.T * d * wl.E if wl.route == "topk" else 0.0),
+        "combine": dict(bytes=served * d * es + 12 * wl.T * wl.k + wl.T * d * es, flops=0.0),
+        "dispatch": dict(bytes=wl.T * d * es + served * d * es + 8 * wl.T * wl.k, flops=0.0),
+    }
+    dom = max(("gemm_up", "gemm_down"), key=lambda n: kern_us[n])
+    dom_us = kern_us[dom]
+    intensity = algo[dom]["flops"] / algo[dom]["bytes"]
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if wl.dtype == "bf16" and intensity >= ridge:
+        bound, achieved, peak, unit = "mfma", algo[dom]["flops"] / dom_us / 1e6, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", algo[dom]["bytes"] / dom_us / 1e3, HBM_PEAK_GBS, "GB/s"
+    kname = {"gemm_up": "ffn_gemm_bf16_kernel (up, act)", "gemm_down": "ffn_gemm_bf16_kernel (down)"}[dom]
+    traffic = read_traffic(dom, wl.name)
+    roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kname,
+                "algorithmic_bytes": int(algo[dom]["bytes"]), "us_per_launch": round(dom_us, 2)}
+    peak_flops = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    kernels = {}
+    for n, us in kern_us.items():
+        row = {"us": round(us, 2)}
+        if n in algo:
+            row["GBps"] = round(algo[n]["bytes"] / us / 1e3, 1)
+            row["hbm_frac"] = round(algo[n]["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4)
+            if algo[n]["flops"]:
+                row["mfma_frac"] = round(algo[n]["flops"] / us / 1e6 / peak_flops, 4)
+        kernels[n] = row
+
+    # ---- CPU baseline: the oracle, on the host cores ----
+    cpu = None
+    if keep_host:
+        cpu = cpu_baseline(wl, inputs, host_w1, host_w2, args.cpu_budget_s)
+
+    out = {
+        "metric": "MoE-layer tokens/sec on 1 MI355X (E=128 top-1); grouped-GEMM MFMA % of peak",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "event_ms_per_step": round(ev_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded: dyadic x and router weight, N(0, 1/fan_in) expert weights)",
+        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d_model, "d_ff": wl.d_ff,
+                   "E": wl.E, "k": wl.k, "capacity_factor": wl.capacity_factor, "act": wl.act,
+                   "route": wl.route, "capacity": C, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "grouped_gemm_mfma_frac": round(2 * algo["gemm_up"]["flops"] /
+                                        ((kern_us["gemm_up"] + kern_us["gemm_down"]) / 1e6) /
+                                        (peak_flops * 1e12), 4),
+        "served_assignments": served,
+        "dropped_assignments": drops,
+        "input_setup_s": round(t_gen, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, inputs, host_w1, host_w2, budget_s):
+    """Time the oracle (as it stands) on the host cores on a bounded sample.
+
+    The sample is the whole workload when it fits the budget, otherwise a
+    prefix of the tokens routed as their own batch (same layer shape).
+    """
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+
+    T = wl.T
+    sample = wl
+    # cost model: ~2.5e10 fp64 flop/s over the host cores; FFN dominates
+    est = 4.0 * wl.T * wl.k * wl.d_model * wl.d_ff / 2.5e10 + 1e-5 * wl.T
+    if est > budget_s:
+        T = max(64, int(wl.T * budget_s / est))
+        sample = wl.replace(T=T)
+    inp = dict(inputs)
+    inp["x"] = inputs["x"][:T]
+    if inputs["group_id"] is not None:
+        inp["group_id"] = inputs["group_id"][:T]
+    inp["w1"], inp["w2"] = host_w1, host_w2
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    oracle.forward(sample, inp)
+    dt = time.perf_counter() - t0
+    desc = ("whole workload" if T == wl.T else f"first {T} of {wl.T} tokens routed as one batch") + \
+        ", float64 NumPy/OpenBLAS oracle: router, dispatch, gather, expert FFN, combine"
+    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": desc, "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

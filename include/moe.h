@@ -153,6 +153,17 @@ int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* expert_idx
 int moe_expert_ffn(const moe_config* cfg, const void* x_e, const int32_t* expert_count,
                    const void* w1, const void* w2, void* y_e, void* ws, void* stream);
 
+/* The two halves of step 4, for callers that keep the hidden activations:
+ *   moe_expert_up:   hidden[e, s] = act(x_e[e, s] W1_e)   (one grouped GEMM launch)
+ *   moe_expert_down: y_e[e, s]    = hidden[e, s] W2_e     (one grouped GEMM launch)
+ * for s < expert_count[e]; hidden is [E, C, d_ff] in dtype (caller-owned device
+ * memory; rows past the count are not written / not read).  moe_expert_ffn is
+ * moe_expert_up followed by moe_expert_down through the workspace. */
+int moe_expert_up(const moe_config* cfg, const void* x_e, const int32_t* expert_count,
+                  const void* w1, void* hidden, void* stream);
+int moe_expert_down(const moe_config* cfg, const void* hidden, const int32_t* expert_count,
+                    const void* w2, void* y_e, void* stream);
+
 /* Step 5, combine.  Switch notes 2.1, Eq. 2: y[t] = sum over c with
  * slot[t, c] >= 0 of gate[t, c] * y_e[expert_idx[t, c], slot[t, c]],
  * accumulated in float32 in choice order; a token with no served choice gets

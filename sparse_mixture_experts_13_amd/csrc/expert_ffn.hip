@@ -251,28 +251,41 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
   return run_bf16<128, 128, 2, 2, ACT>(p.E, A, W, out, count, p.C, N, K, s);
 }
 
-hipError_t launch_expert_ffn(const Plan& p, const void* x_e, const int32_t* expert_count,
-                             const void* w1, const void* w2, void* y_e, void* ws, hipStream_t s) {
+hipError_t launch_expert_up(const Plan& p, const void* x_e, const int32_t* expert_count,
+                            const void* w1, void* hidden, hipStream_t s) {
   if (p.C == 0) return hipSuccess;
-  void* hidden = ws_at(ws, p.off_region[6]);
   const int d = static_cast<int>(p.d), f = static_cast<int>(p.f);
-  hipError_t err;
   if (p.dtype == 1) {
     const bf16_t* xe = static_cast<const bf16_t*>(x_e);
+    const bf16_t* w = static_cast<const bf16_t*>(w1);
     bf16_t* h = static_cast<bf16_t*>(hidden);
-    if (p.act == 0) err = gemm_bf16<0>(p, xe, static_cast<const bf16_t*>(w1), h, expert_count, f, d, s);
-    else err = gemm_bf16<1>(p, xe, static_cast<const bf16_t*>(w1), h, expert_count, f, d, s);
-    if (err != hipSuccess) return err;
-    return gemm_bf16<2>(p, h, static_cast<const bf16_t*>(w2), static_cast<bf16_t*>(y_e),
-                        expert_count, d, f, s);
+    return p.act == 0 ? gemm_bf16<0>(p, xe, w, h, expert_count, f, d, s)
+                      : gemm_bf16<1>(p, xe, w, h, expert_count, f, d, s);
   }
   const float* xe = static_cast<const float*>(x_e);
+  const float* w = static_cast<const float*>(w1);
   float* h = static_cast<float*>(hidden);
-  if (p.act == 0) err = run_f32<0>(p.E, xe, static_cast<const float*>(w1), h, expert_count, p.C, f, d, s);
-  else err = run_f32<1>(p.E, xe, static_cast<const float*>(w1), h, expert_count, p.C, f, d, s);
+  return p.act == 0 ? run_f32<0>(p.E, xe, w, h, expert_count, p.C, f, d, s)
+                    : run_f32<1>(p.E, xe, w, h, expert_count, p.C, f, d, s);
+}
+
+hipError_t launch_expert_down(const Plan& p, const void* hidden, const int32_t* expert_count,
+                              const void* w2, void* y_e, hipStream_t s) {
+  if (p.C == 0) return hipSuccess;
+  const int d = static_cast<int>(p.d), f = static_cast<int>(p.f);
+  if (p.dtype == 1)
+    return gemm_bf16<2>(p, static_cast<const bf16_t*>(hidden), static_cast<const bf16_t*>(w2),
+                        static_cast<bf16_t*>(y_e), expert_count, d, f, s);
+  return run_f32<2>(p.E, static_cast<const float*>(hidden), static_cast<const float*>(w2),
+                    static_cast<float*>(y_e), expert_count, p.C, d, f, s);
+}
+
+hipError_t launch_expert_ffn(const Plan& p, const void* x_e, const int32_t* expert_count,
+                             const void* w1, const void* w2, void* y_e, void* ws, hipStream_t s) {
+  void* hidden = ws_at(ws, p.off_region[6]);
+  const hipError_t err = launch_expert_up(p, x_e, expert_count, w1, hidden, s);
   if (err != hipSuccess) return err;
-  return run_f32<2>(p.E, h, static_cast<const float*>(w2), static_cast<float*>(y_e), expert_count,
-                    p.C, d, f, s);
+  return launch_expert_down(p, hidden, expert_count, w2, y_e, s);
 }
 
 }  // namespace moe

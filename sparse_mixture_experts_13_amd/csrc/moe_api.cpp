@@ -244,6 +244,36 @@ int moe_expert_ffn(const moe_config* cfg, const void* x_e, const int32_t* expert
   return MOE_OK;
 }
 
+int moe_expert_up(const moe_config* cfg, const void* x_e, const int32_t* expert_count,
+                  const void* w1, void* hidden, void* stream) {
+  MOE_CHECK(validate(cfg));
+  moe::Plan p;
+  make_plan(cfg, p);
+  const int64_t EC = int64_t(p.E) * p.C;
+  MOE_CHECK(need(x_e, EC * p.d * p.elem, "x_e"));
+  MOE_CHECK(need(expert_count, int64_t(p.E) * 4, "expert_count"));
+  MOE_CHECK(need(w1, int64_t(p.E) * p.d * p.f * p.elem, "w1"));
+  MOE_CHECK(need(hidden, EC * p.f * p.elem, "hidden"));
+  MOE_HIP(moe::launch_expert_up(p, x_e, expert_count, w1, hidden, static_cast<hipStream_t>(stream)),
+          "expert up-projection");
+  return MOE_OK;
+}
+
+int moe_expert_down(const moe_config* cfg, const void* hidden, const int32_t* expert_count,
+                    const void* w2, void* y_e, void* stream) {
+  MOE_CHECK(validate(cfg));
+  moe::Plan p;
+  make_plan(cfg, p);
+  const int64_t EC = int64_t(p.E) * p.C;
+  MOE_CHECK(need(hidden, EC * p.f * p.elem, "hidden"));
+  MOE_CHECK(need(expert_count, int64_t(p.E) * 4, "expert_count"));
+  MOE_CHECK(need(w2, int64_t(p.E) * p.d * p.f * p.elem, "w2"));
+  MOE_CHECK(need(y_e, EC * p.d * p.elem, "y_e"));
+  MOE_HIP(moe::launch_expert_down(p, hidden, expert_count, w2, y_e, static_cast<hipStream_t>(stream)),
+          "expert down-projection");
+  return MOE_OK;
+}
+
 int moe_combine(const moe_config* cfg, const void* y_e, const int32_t* expert_idx,
                 const int32_t* slot, const float* gate, void* y, void* stream) {
   MOE_CHECK(validate(cfg));

@@ -41,6 +41,10 @@ hipError_t launch_dispatch_slot_gather(const Plan& p, const void* x, const int32
 // expert_ffn.hip
 hipError_t launch_expert_ffn(const Plan& p, const void* x_e, const int32_t* expert_count,
                              const void* w1, const void* w2, void* y_e, void* ws, hipStream_t s);
+hipError_t launch_expert_up(const Plan& p, const void* x_e, const int32_t* expert_count,
+                            const void* w1, void* hidden, hipStream_t s);
+hipError_t launch_expert_down(const Plan& p, const void* hidden, const int32_t* expert_count,
+                              const void* w2, void* y_e, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const Plan& p, const void* y_e, const int32_t* expert_idx,
