@@ -4,7 +4,7 @@
 // Order: assignments are placed choice by choice and, inside a choice, in token
 // order, so the slot of (token t, choice c) in expert e is the number of earlier
 // assignments to e in that order.  Computed without atomics on global memory in
-// three phases over blocks of 64 tokens (the router's blocks):
+// three phases over the router's blocks of TB tokens:
 //   1. per-block histogram hist[e][c][b] (the router epilogue writes it; the
 //      stand-alone dispatch recomputes it from expert_idx);
 //   2. one wave per expert: exclusive scan of hist[e][*][*] in (choice, block)
@@ -19,16 +19,16 @@
 
 namespace moe {
 
-// Phase 1 (stand-alone dispatch): one 256-thread block per 64-token block.
+// Phase 1 (stand-alone dispatch): one 256-thread block per router block of TB tokens.
 __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ expert_idx,
-                                                            int T, int E, int k, int NB,
+                                                            int T, int E, int k, int NB, int TB,
                                                             int* __restrict__ hist) {
   __shared__ int hl[kMaxK * kMaxE];
   const int tid = threadIdx.x, b = blockIdx.x;
   for (int i = tid; i < k * E; i += 256) hl[i] = 0;
   __syncthreads();
-  const int t0 = b * 64;
-  const int n = min(64, T - t0) * k;
+  const int t0 = b * TB;
+  const int n = min(TB, T - t0) * k;
   for (int i = tid; i < n; i += 256) {
     const int e = expert_idx[static_cast<int64_t>(t0) * k + i];
     const int c = i % k;
@@ -70,21 +70,21 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int* __restric
   for (int64_t s = cnt + lane; s < C; s += kWave) slot_token[e * C + s] = -1;
 }
 
-// Phase 3: 16 tokens per 256-thread block (four blocks share one 64-token
-// router block); VEC = 16-byte vectors per row.
+// Phase 3: 16 tokens per 256-thread block (TB / 16 blocks share one router
+// block of TB tokens).
 constexpr int kSlotTokens = 16;
 
 __global__ __launch_bounds__(256) void dispatch_slot_gather_kernel(
     const uint8_t* __restrict__ x, const int32_t* __restrict__ expert_idx, int T, int E, int k,
-    int NB, int64_t C, int64_t row_bytes, const int* __restrict__ offsets,
+    int NB, int TB, int64_t C, int64_t row_bytes, const int* __restrict__ offsets,
     int32_t* __restrict__ slot, int32_t* __restrict__ slot_token, uint8_t* __restrict__ x_e) {
-  __shared__ int sidx[64 * kMaxK];
+  __shared__ int sidx[kMaxRouterBlock * kMaxK];
   __shared__ int dst_e[kSlotTokens * kMaxK];
   __shared__ int dst_s[kSlotTokens * kMaxK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kSlotTokens;
-  const int b = t0 / 64;
-  const int blk0 = b * 64;
+  const int b = t0 / TB;
+  const int blk0 = b * TB;
   const int tend = min(t0 + kSlotTokens, T);
   // expert choices of the router block up to the end of this group
   for (int i = tid; i < (tend - blk0) * k; i += 256)
@@ -137,7 +137,7 @@ hipError_t launch_dispatch_hist(const Plan& p, const int32_t* expert_idx, void* 
   if (p.T == 0) return hipSuccess;
   int* hist = reinterpret_cast<int*>(ws_at(ws, p.off_hist));
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(p.NB), dim3(256), 0, s, expert_idx,
-                     static_cast<int>(p.T), p.E, p.k, p.NB, hist);
+                     static_cast<int>(p.T), p.E, p.k, p.NB, p.TB, hist);
   return hipGetLastError();
 }
 
@@ -158,7 +158,7 @@ hipError_t launch_dispatch_slot_gather(const Plan& p, const void* x, const int32
   const int nblk = static_cast<int>((p.T + kSlotTokens - 1) / kSlotTokens);
   hipLaunchKernelGGL(dispatch_slot_gather_kernel, dim3(nblk), dim3(256), 0, s,
                      static_cast<const uint8_t*>(x), expert_idx, static_cast<int>(p.T), p.E, p.k,
-                     p.NB, p.C, p.d * p.elem, offsets, slot, slot_token,
+                     p.NB, p.TB, p.C, p.d * p.elem, offsets, slot, slot_token,
                      static_cast<uint8_t*>(x_e));
   return hipGetLastError();
 }

@@ -5,16 +5,13 @@
 //
 // Two launches of one grouped GEMM: hidden = act(x_e . w1[e]^T), then
 // y_e = hidden . w2[e]^T.  Both operands are stored K-contiguous (activations
-// [E][C][K], weights [E][N][K]), so the MFMA A and B fragments are 16-byte row
-// reads.  The kernel computes the transposed tile D = W . X^T so that each lane
-// ends with four consecutive output columns of one row (8-byte stores).
-//
-// gfx950: v_mfma_f32_32x32x16_bf16 with float32 accumulation; LDS-staged,
-// double-buffered tiles (BK = 64, rows padded to 144 bytes so the fragment reads
-// are bank-conflict free); one block per (expert, row tile, column tile); tiles
-// whose first row is past the expert's token count exit at once, so the grid is
-// static (no device-to-host read of the counts) while dropped capacity costs no
-// MFMA work.  float32 workloads use a plain float32 FMA tile kernel.
+// [E][C][K], weights [E][N][K]).  The kernel computes the transposed tile
+// D = W . X^T so that each lane ends with four consecutive output columns of
+// one row (8-byte stores).  bf16 runs on v_mfma_f32_32x32x16_bf16 with float32
+// accumulation in a persistent kernel over the non-empty tiles only, so the
+// grid is fixed (no device-to-host read of the counts) while dropped or unused
+// capacity costs neither bandwidth nor MFMA work.  float32 workloads use a
+// plain float32 FMA tile kernel.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -30,6 +27,10 @@ __host__ __device__ constexpr int ffn_lds_bytes() {
   return 2 * (BM + BN) * GLD * 2;
 }
 
+// LDS-tiled grouped GEMM for large capacities: one block per (expert, row
+// tile, column tile) of BM x BN, register-staged double-buffered LDS tiles
+// (BK = 64, rows padded to 144 bytes: conflict-free fragment reads); tiles past
+// the expert's count exit at once.
 template <int BM, int BN, int WM, int WN, int ACT>
 __global__ __launch_bounds__(256) void ffn_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
@@ -150,6 +151,225 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Persistent grouped GEMM on bf16 MFMA with a direct-to-LDS stage ring.
+//
+// Tiles are (expert e, row block mb, column block nb) of BM x BN outputs,
+// BM = WM * TM * 32 activation rows and BN = WN * TN * 32 weight rows; wave
+// (wm, wn) of the WM x WN wave grid owns TM x TN MFMA tiles of 32 x 32.  Only
+// tiles holding tokens exist (expert e has ceil(count[e] / BM) row blocks), and
+// each block takes an equal contiguous share of them, in (e, mb, nb) order.
+//
+// A block streams its share as one sequence of 64-k stages:
+//   * stages land in an S-deep LDS ring through direct global->LDS 16-byte
+//     loads issued S-1 stages ahead, across tile boundaries (no per-tile
+//     pipeline fill); weight loads are non-temporal when a weight tile is
+//     read by one row block only (each byte read once per launch), and every
+//     wave instruction covers whole 128-byte row segments;
+//   * LDS rows are 128 bytes with the 16-byte chunk index XORed by
+//     (row / 2) % 8, so the MFMA fragment reads hit distinct banks;
+//   * blocks are renumbered so that consecutive shares (mostly one expert)
+//     run on one XCD and share activations and weights in that L2.
+// Rows past the expert's count (and weight rows past N) are loaded from a
+// clamped valid row: their products land only in outputs that are never
+// stored, so every stage issues the same number of loads and the wait for a
+// stage is a fixed memory-counter threshold.
+// Inside a 64-k stage, MFMA j (j = 0..3) of lane half h contracts the 16-byte
+// chunk 2j + h of each row: A and B fragments use the same k assignment.
+// ---------------------------------------------------------------------------
+// LDS: stage ring | tile prefix per expert
+template <int TM, int TN, int WM, int WN, int S, int BK>
+__host__ __device__ constexpr int ffn_ring_lds_bytes() {
+  return S * (WN * TN * 32 + WM * TM * 32) * BK * 2 + (kMaxE + 1) * 4;
+}
+
+template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT>
+__global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
+    const int32_t* __restrict__ count, int E, int64_t C, int N, int K) {
+  constexpr int NW = WM * WN;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int RB = BK * 2;         // LDS row bytes
+  constexpr int CPR = BK / 8;        // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;     // rows per wave instruction (64 lanes x 16 bytes)
+  constexpr int WL = BN / RPI / NW;  // direct-to-LDS instructions per wave per stage (weights)
+  constexpr int AL = BM / RPI / NW;  // ... (activations)
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(BN % (RPI * NW) == 0 && BM % (RPI * NW) == 0 && AL >= 1, "stage split");
+  constexpr int STAGE = (BN + BM) * RB;
+  constexpr int PER_STAGE = WL + AL;
+  static_assert((S - 2) * PER_STAGE < 64, "memory counter range");
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* pre = reinterpret_cast<int*>(smem + S * STAGE);  // [E + 1] tile prefix per expert
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+  const int half = lane >> 5, fr = lane & 31;
+  const int n_nb = (N + BN - 1) / BN;
+  const int KS = K / BK;
+
+  auto rows_of = [&](int e) {
+    int64_t c = count[e];
+    return static_cast<int>(c < 0 ? 0 : (c > C ? C : c));
+  };
+  // prefix of non-empty tiles over experts (wave 0), shared through LDS
+  if (wave == 0) {
+    int run = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+      const int e = e0 + lane;
+      const int t = e < E ? (rows_of(e) + BM - 1) / BM * n_nb : 0;
+      const int incl = wave_inclusive_scan(t, lane) + run;
+      if (e < E) pre[e + 1] = incl;
+      run = __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) pre[0] = 0;
+  }
+  __syncthreads();
+  const int V = pre[E];
+  const int G = gridDim.x;
+  const int g = xcd_major_id(blockIdx.x, G);
+  const int v0 = static_cast<int>(static_cast<int64_t>(g) * V / G);
+  const int v1 = static_cast<int>(static_cast<int64_t>(g + 1) * V / G);
+  const int total = (v1 - v0) * KS;
+  if (total == 0) return;
+
+  // a tile cursor: expert, row block, column block of linear non-empty tile v
+  struct Cur { int v, e, mb, nb, cnt; };
+  auto seek = [&](Cur& c, int v) {
+    c.v = v;
+    int e = 0;
+    while (pre[e + 1] <= v) ++e;
+    const int local = v - pre[e];
+    c.e = e;
+    c.mb = local / n_nb;
+    c.nb = local - c.mb * n_nb;
+    c.cnt = rows_of(e);
+  };
+  auto next = [&](Cur& c) {
+    ++c.v;
+    if (++c.nb == n_nb) {
+      c.nb = 0;
+      ++c.mb;
+      if (c.v < pre[c.e + 1]) return;
+      do { ++c.e; } while (c.e < E && pre[c.e + 1] <= c.v);
+      c.mb = 0;
+      if (c.e < E) c.cnt = rows_of(c.e);
+    }
+  };
+
+  Cur lc, cc;
+  seek(lc, v0);
+  cc = lc;
+  int lk = 0;
+  // Loads use a block-uniform per-expert base plus 32-bit lane offsets.
+  auto issue = [&](int slot) {
+    const int n0 = lc.nb * BN, m0 = lc.mb * BM;
+    unsigned char* base = smem + slot * STAGE;
+    const bf16_t* We = W + static_cast<int64_t>(lc.e) * N * K;
+    const bf16_t* Ae = A + static_cast<int64_t>(lc.e) * C * K;
+#pragma unroll
+    for (int q = 0; q < WL; ++q) {
+      const int p = (wave * WL + q) * 64 + lane;
+      const int row = p / CPR;
+      const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
+      const uint32_t off = static_cast<uint32_t>(min(n0 + row, N - 1)) * K + lk * BK + c * 8;
+      // non-temporal when each weight tile is read by one row block only
+      __builtin_amdgcn_global_load_lds(We + off, (lds_void*)(base + (wave * WL + q) * 1024), 16, 0,
+                                       NTW ? 2 : 0);
+    }
+    unsigned char* abase = base + BN * RB;
+#pragma unroll
+    for (int q = 0; q < AL; ++q) {
+      const int p = (wave * AL + q) * 64 + lane;
+      const int row = p / CPR;
+      const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
+      const uint32_t off = static_cast<uint32_t>(min(m0 + row, lc.cnt - 1)) * K + lk * BK + c * 8;
+      __builtin_amdgcn_global_load_lds(Ae + off, (lds_void*)(abase + (wave * AL + q) * 1024), 16, 0, 0);
+    }
+    if (++lk == KS) {
+      lk = 0;
+      next(lc);
+    }
+  };
+
+  floatx16 acc[TN][TM];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
+  };
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i)
+    if (i < total) issue(i);
+  int s = 0;  // stage index over the block's whole sequence
+  for (int tile = v0; tile < v1; ++tile) {
+    zero_acc();
+    for (int kk = 0; kk < KS; ++kk, ++s) {
+      if (total - 1 - s >= S - 2) wait_vmcnt<(S - 2) * PER_STAGE>();
+      else wait_vmcnt<0>();
+      ring_barrier();
+      if (s + S - 1 < total) issue((s + S - 1) % S);
+      const unsigned char* sw = smem + (s % S) * STAGE;
+      const unsigned char* sa = sw + BN * RB;
+      // fragments of sub-step j + 1 load while sub-step j's MFMAs run
+      bf16x8 fa[2][TN], fb[2][TM];
+      auto load_frags = [&](int j, int buf) {
+        const int c = 2 * j + half;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+          const int row = (wm * TM + t) * 32 + fr;
+          fb[buf][t] = *reinterpret_cast<const bf16x8*>(sa + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
+        }
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const int row = (wn * TN + i) * 32 + fr;
+          fa[buf][i] = *reinterpret_cast<const bf16x8*>(sw + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
+        }
+      };
+      constexpr int NJ = BK / 16;  // MFMA sub-steps per stage
+      load_frags(0, 0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (j + 1 < NJ) load_frags(j + 1, (j + 1) & 1);
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int t = 0; t < TM; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j & 1][i], fb[j & 1][t], acc[i][t], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // tile done: D[n][m], lane holds m = lane % 32 and four consecutive n per group
+    const int m0 = cc.mb * BM, n0 = cc.nb * BN;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const int m = m0 + (wm * TM + t) * 32 + fr;
+      if (m < cc.cnt) {
+        bf16_t* orow = out + (static_cast<int64_t>(cc.e) * C + m) * N;
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const int nt0 = n0 + (wn * TN + i) * 32;
+          if (nt0 < N) {  // N % 32 == 0: a 32-column tile is wholly valid or not
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int n = nt0 + 8 * q + 4 * half;
+              uint2 v;
+              v.x = pack_bf16x2(apply_act<ACT>(acc[i][t][4 * q]), apply_act<ACT>(acc[i][t][4 * q + 1]));
+              v.y = pack_bf16x2(apply_act<ACT>(acc[i][t][4 * q + 2]), apply_act<ACT>(acc[i][t][4 * q + 3]));
+              *reinterpret_cast<uint2*>(orow + n) = v;
+            }
+          }
+        }
+      }
+    }
+    next(cc);
+  }
+}
+
 // float32 grouped GEMM: 64 x 64 tile, 4 x 4 outputs per thread, BK = 16.
 template <int ACT>
 __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(const float* __restrict__ A,
@@ -232,6 +452,23 @@ static hipError_t run_bf16(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
   return hipGetLastError();
 }
 
+template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT>
+static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
+                           const int32_t* count, int64_t C, int N, int K, hipStream_t s) {
+  auto kern = ffn_ring_bf16_kernel<TM, TN, WM, WN, S, BK, NTW, ACT>;
+  constexpr int lds = ffn_ring_lds_bytes<TM, TN, WM, WN, S, BK>();
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err != hipSuccess) return err;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  const int64_t tiles = static_cast<int64_t>(E) * ((C + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles == 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>(tiles, 256);  // one persistent block per CU
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), lds, s, A, W,
+                     out, count, E, C, N, K);
+  return hipGetLastError();
+}
+
 template <int ACT>
 static hipError_t run_f32(int E, const float* A, const float* W, float* out, const int32_t* count,
                           int64_t C, int N, int K, hipStream_t s) {
@@ -244,10 +481,16 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
   return hipGetLastError();
 }
 
+// Tile shapes by capacity.  Capacity <= 160: one row block holds every token of
+// an expert, so the GEMM is bound by streaming the weights once: persistent
+// direct-to-LDS ring kernel (8 or 4 waves, 256 weight rows per tile, 3-stage
+// ring).  Larger capacities: LDS-tiled 128 x 128 kernel.
 template <int ACT>
 static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf16_t* out,
                             const int32_t* count, int N, int K, hipStream_t s) {
-  if (p.C <= 64) return run_bf16<64, 128, 1, 4, ACT>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C <= 128) return run_ring<4, 1, 1, 8, 3, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C <= 160) return run_ring<5, 2, 1, 4, 3, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
   return run_bf16<128, 128, 2, 2, ACT>(p.E, A, W, out, count, p.C, N, K, s);
 }
 

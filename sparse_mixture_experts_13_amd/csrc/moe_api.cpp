@@ -89,7 +89,16 @@ void make_plan(const moe_config* cfg, moe::Plan& p) {
   p.k = cfg->k;
   p.C = exact_capacity(cfg->T, cfg->E, cfg->k, cfg->capacity_factor);
   p.Epad = (cfg->E + 31) / 32 * 32;
-  p.NB = static_cast<int>((cfg->T + moe::kRouterBlock - 1) / moe::kRouterBlock);
+  // Router block: the bf16 MFMA router takes 32, 64 or 128 tokens per block,
+  // aiming at >= 256 blocks (one per CU) and at most 32 tokens when E > 256;
+  // the other routers use 64.
+  p.TB = 64;
+  if (cfg->route == MOE_ROUTE_TOPK && cfg->dtype == MOE_DTYPE_BF16) {
+    const int64_t per_cu = cfg->T / 256;
+    p.TB = per_cu >= 128 ? 128 : (per_cu >= 64 ? 64 : 32);
+    if (p.Epad > 256) p.TB = 32;
+  }
+  p.NB = static_cast<int>((cfg->T + p.TB - 1) / p.TB);
   p.dtype = cfg->dtype;
   p.act = cfg->act;
   p.route = cfg->route;

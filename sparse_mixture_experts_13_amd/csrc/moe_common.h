@@ -82,4 +82,63 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
+// Renumber block b of nblk so that blocks b, b+8, b+16, ... (which the
+// dispatcher places on one XCD, round robin) get consecutive ids.
+__device__ __forceinline__ int xcd_major_id(int b, int nblk) {
+  const int q = nblk / 8, r = nblk % 8;
+  const int x = b % 8, j = b / 8;
+  const int base = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+  return base + j;
+}
+
+// ---- LDS stage rings fed by direct global->LDS loads ----
+// Rows of 128 bytes (64 bf16); the 16-byte chunk index is XORed with
+// (row / 2) % 8 so that sixteen consecutive rows read at one chunk position
+// fall in distinct banks.
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
+
+// Same for rows of CPR 16-byte chunks: 8 chunks (128-byte rows) XOR (row/2)%8,
+// 4 chunks (64-byte rows) XOR (row/4)%4; either way sixteen consecutive rows
+// at one chunk position cover sixteen distinct 16-byte bank groups.
+template <int CPR>
+__device__ __forceinline__ int lds_swz_n(int row) {
+  if constexpr (CPR == 8) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n known only at run time (0 <= n < 64).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+#define MOE_W1(i) case i: wait_vmcnt<i>(); break;
+#define MOE_W4(i) MOE_W1(i) MOE_W1(i + 1) MOE_W1(i + 2) MOE_W1(i + 3)
+#define MOE_W16(i) MOE_W4(i) MOE_W4(i + 4) MOE_W4(i + 8) MOE_W4(i + 12)
+    MOE_W16(0) MOE_W16(16) MOE_W16(32) MOE_W16(48)
+#undef MOE_W16
+#undef MOE_W4
+#undef MOE_W1
+    default: wait_vmcnt<0>();
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Work-group barrier for the stage ring.  It must not drain the prefetched
+// direct-to-LDS loads (a fenced __syncthreads() waits for all of them), so it
+// is a bare s_barrier after this wave's own LDS reads have completed; the
+// stage data itself is covered by the explicit memory-counter wait before it.
+// LDS reads of a stage feed MFMAs of the same iteration, and the next LDS
+// write to that slot is a load issued after the barrier, which the compiler
+// does not move above it.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), other counters unconstrained
+  __builtin_amdgcn_s_barrier();
+}
+
 }  // namespace moe

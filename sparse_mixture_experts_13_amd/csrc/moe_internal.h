@@ -6,7 +6,7 @@
 
 namespace moe {
 
-constexpr int kRouterBlock = 64;   // tokens per router block (histogram granularity)
+constexpr int kMaxRouterBlock = 128;  // tokens per router block (histogram granularity): 32, 64 or 128
 constexpr int kMaxE = 512;
 constexpr int kMaxK = 8;
 constexpr int kSplitBlocks = 64;   // blocks of the router-weight split kernel
@@ -14,7 +14,8 @@ constexpr int kSplitBlocks = 64;   // blocks of the router-weight split kernel
 // Sizes derived once from a validated configuration.
 struct Plan {
   int64_t T, d, f, C;
-  int E, k, Epad, NB;      // Epad: E rounded up to 32; NB: router blocks of 64 tokens
+  int E, k, Epad, NB;      // Epad: E rounded up to 32; NB: router blocks of TB tokens
+  int TB;                  // tokens per router block
   int dtype, act, route, n_groups;
   uint64_t rre_seed;
   int elem;                // bytes per element of dtype

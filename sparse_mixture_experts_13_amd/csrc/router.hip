@@ -7,15 +7,17 @@
 // top-1/top-2 routing (TorchScale review).  Random Routed Experts (PanGu-Sigma
 // review): a uniform pick inside the token's expert group, no learned gate.
 //
-// gfx950 design.  A work-group owns 64 tokens.  The logits tile [64 x E] is a
-// skinny GEMM done on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with float32
-// accumulation: x is bf16 already, and the float32 router weight is split once
-// per call into three bf16 planes hi + mid + lo that sum to it exactly, so every
-// product is exact; when the weight is bf16-exact (mid = lo = 0, detected on the
-// device) only the hi plane is used.  Token and weight tiles are staged in LDS
-// (double-buffered); the logits tile then goes to LDS and each wave ranks whole
-// tokens with 64-bit keys (logit, then lower index) reduced across the wave.
-// The expert histogram of the block is built in LDS for the dispatch scan.
+// gfx950 design (bf16 tokens).  A work-group owns a block of TB tokens (32,
+// 64 or 128) and every expert.  The logits tile [TB x E] is a skinny GEMM on
+// bf16 MFMA (v_mfma_f32_32x32x16_bf16) with float32 accumulation: x is bf16
+// already, and the float32 router weight is split once per call into three
+// bf16 planes hi + mid + lo that sum to it exactly, so every product is exact;
+// when the weight is bf16-exact (mid = lo = 0, detected on the device) only the
+// hi plane is used.  Weight and token rows stream through an LDS stage ring fed
+// by direct global->LDS loads; the logits tile then goes to LDS, and sixteen
+// lanes rank each token with 64-bit keys (logit, then lower index).  The block's
+// expert histogram is built in LDS for the dispatch scan.  float32 tokens use a
+// float32 FMA kernel with the same ranking, 64 tokens per block.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -131,124 +133,184 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 
 // ---------------------------------------------------------------------------
 // bf16 router: MFMA logits tile + top-k epilogue.
+//
+// A block owns TB = 32 * TT tokens and all experts.  Each 64-k stage (router
+// weight rows 0..Epad-1, then the block's TB token rows, 128 bytes each) lands
+// in an S-deep LDS ring through direct global->LDS loads issued S-1 stages
+// ahead; for a non-bf16-exact weight the stages run over the hi, mid and lo
+// planes in turn.  Wave w owns expert tiles w, w+4, ... (up to EW of them)
+// against every token tile: D = W_r . x^T with v_mfma_f32_32x32x16_bf16.
 // ---------------------------------------------------------------------------
-constexpr int RBK = 32;        // k elements per LDS stage
-constexpr int RLD = RBK + 8;   // padded LDS row, bf16 elements (80 bytes: conflict-free frags)
-
-__host__ __device__ inline int64_t router_bf16_stage_bytes(int Epad) {
-  return 2LL * (64 + Epad) * RLD * 2;
+__host__ __device__ inline int64_t router_ring_bytes(int Epad, int TB, int S) {
+  return static_cast<int64_t>(S) * (Epad + TB) * 128;
 }
-__host__ __device__ inline int64_t router_lg_bytes(int Epad) { return 64LL * (Epad + 4) * 4; }
+__host__ __device__ inline int64_t router_lg_bytes(int TB, int Epad) {
+  return static_cast<int64_t>(TB) * (Epad + 4) * 4;
+}
 
-// MAXU: expert tiles of 32 per wave (wave w owns tiles w, w+4, ...); Epad <= 128 * MAXU.
-template <int MAXU>
+// Rank the tokens of a block from the logits tile lg [TB][ld] in LDS.  Sixteen
+// lanes share a token (a wave ranks four tokens at a time); lane `sub` holds
+// experts sub, sub+16, ...  Keys order by (logit desc, expert asc).
+template <int NV>
+__device__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int ntok, int E, int k,
+                                const float* __restrict__ bias, int32_t* __restrict__ expert_idx,
+                                float* __restrict__ gate, int* hl, int ldh, int wave, int lane) {
+  const int grp = lane >> 4, sub = lane & 15;
+  for (int base = 0; base < TB; base += 16) {
+    const int t = base + wave * 4 + grp;
+    const bool valid = t < ntok;
+    float hv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = sub + 16 * i;
+      hv[i] = -INFINITY;
+      if (valid && e < E) {
+        float h = lg[t * ld + e];
+        if (bias) h = h + bias[e];  // one float32 rounding after the full dot product
+        hv[i] = h;
+      }
+    }
+    uint32_t removed = 0;
+    uint64_t best0 = 0, mine = 0;
+    for (int c = 0; c < k; ++c) {
+      uint64_t m = 0;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = sub + 16 * i;
+        const uint64_t key = (e < E && !((removed >> i) & 1u)) ? make_key(hv[i], e) : 0ull;
+        m = key > m ? key : m;
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const uint64_t w = __shfl_xor(m, o, kWave);
+        m = w > m ? w : m;
+      }
+      const int ew = key_expert(m);
+      if ((ew & 15) == sub) removed |= 1u << (ew >> 4);
+      if (c == 0) best0 = m;
+      if (sub == c) mine = m;
+    }
+    const float hmax = key_logit(best0);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sum += expf(hv[i] - hmax);  // exp(-inf) = 0
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+    if (valid && sub < k) {
+      const int e = key_expert(mine);
+      const int64_t o = static_cast<int64_t>(tok0 + t) * k + sub;
+      expert_idx[o] = e;
+      gate[o] = expf(key_logit(mine) - hmax) / sum;
+      atomicAdd(&hl[sub * ldh + e], 1);
+    }
+  }
+}
+
+template <int TT, int EW, int S>
 __global__ __launch_bounds__(256) void router_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, const int* __restrict__ flags,
     const float* __restrict__ bias, int T, int d, int E, int Epad, int k,
     int32_t* __restrict__ expert_idx, float* __restrict__ gate, int* __restrict__ hist, int NB) {
+  constexpr int TB = 32 * TT;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, fr = lane & 31;
   const int b = blockIdx.x;
-  const int tok0 = b * 64;
-  const int ntok = min(64, T - tok0);
+  const int tok0 = b * TB;
+  const int ntok = min(TB, T - tok0);
   const int n_et = Epad / 32;
-
-  bf16_t* sx = reinterpret_cast<bf16_t*>(smem);   // [2][64][RLD]
-  bf16_t* sw = sx + 2 * 64 * RLD;                 // [2][Epad][RLD]
-  float* lg = reinterpret_cast<float*>(smem);     // [64][Epad + 4], after the K loop
-  const int64_t body = max(router_bf16_stage_bytes(Epad), router_lg_bytes(Epad));
+  const int rows = Epad + TB;
+  const int R = rows / 32;  // direct-to-LDS instructions per thread per stage
+  const int64_t STAGE = static_cast<int64_t>(rows) * 128;
+  const int64_t body = max(router_ring_bytes(Epad, TB, S), router_lg_bytes(TB, Epad));
   int* hl = reinterpret_cast<int*>(smem + body);  // [k][Epad]
-
   for (int i = tid; i < k * Epad; i += 256) hl[i] = 0;
 
   int any = 0;
   for (int i = 0; i < kSplitBlocks; ++i) any |= flags[i];
-  const int nplanes = any ? 3 : 1;
-  const int KT = d / RBK;
-  const int nsteps = nplanes * KT;
+  const int KS = d / 64;
+  const int total = (any ? 3 : 1) * KS;
   const int64_t plane_elems = static_cast<int64_t>(Epad) * d;
 
-  floatx16 acc[MAXU][2];
+  // Blocks start their k loop at different offsets so that they do not all
+  // read the same router-weight rows at the same moment (hot L2 channels).
+  const int rot = b % KS;
+  auto issue = [&](int st, int slot) {
+    const int p = st / KS;
+    int ks = st - p * KS + rot;
+    ks = ks >= KS ? ks - KS : ks;
+    const bf16_t* wp = planes + p * plane_elems;
+    unsigned char* base = smem + slot * STAGE;
+    for (int q = 0; q < R; ++q) {
+      const int rbase = (q * 4 + wave) * 8;  // first of the 8 rows this wave loads
+      const int row = rbase + (lane >> 3);
+      const int c = (lane & 7) ^ lds_swz(row);
+      const bf16_t* src;
+      if (rbase < Epad) {
+        src = wp + static_cast<int64_t>(row) * d + ks * 64 + c * 8;
+      } else {
+        const int t = min(tok0 + row - Epad, T - 1);
+        src = x + static_cast<int64_t>(t) * d + ks * 64 + c * 8;
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + (q * 4 + wave) * 1024), 16, 0, 0);
+    }
+  };
+
+  floatx16 acc[EW][TT];
 #pragma unroll
-  for (int u = 0; u < MAXU; ++u)
+  for (int u = 0; u < EW; ++u)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[u][tt][r] = 0.f;
 
-  u32x4 rx;
-  u32x4 rw[2 * MAXU];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  const int xr = tid >> 2, xc = tid & 3;
-  const int tx = tok0 + xr;
-
-  auto gload = [&](int step) {
-    const int p = step / KT;
-    const int k0 = (step - p * KT) * RBK;
-    rx = tx < T ? *reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(tx) * d + k0 + xc * 8)
-                : zero4;
-    const bf16_t* wp = planes + p * plane_elems;
 #pragma unroll
-    for (int i = 0; i < 2 * MAXU; ++i) {
-      const int id = tid + 256 * i;
-      if (id < Epad * 4) {
-        const int row = id >> 2, c = id & 3;
-        rw[i] = *reinterpret_cast<const u32x4*>(wp + static_cast<int64_t>(row) * d + k0 + c * 8);
+  for (int i = 0; i < S - 1; ++i)
+    if (i < total) issue(i, i);
+  for (int st = 0; st < total; ++st) {
+    wait_vmcnt_dyn(total - 1 - st >= S - 2 ? (S - 2) * R : 0);
+    ring_barrier();
+    if (st + S - 1 < total) issue(st + S - 1, (st + S - 1) % S);
+    const unsigned char* sb = smem + (st % S) * STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 2 * j + half;
+      bf16x8 bq[TT];
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int row = Epad + tt * 32 + fr;
+        bq[tt] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
       }
-    }
-  };
-  auto sstore = [&](int buf) {
-    *reinterpret_cast<u32x4*>(sx + (buf * 64 + xr) * RLD + xc * 8) = rx;
 #pragma unroll
-    for (int i = 0; i < 2 * MAXU; ++i) {
-      const int id = tid + 256 * i;
-      if (id < Epad * 4) {
-        const int row = id >> 2, c = id & 3;
-        *reinterpret_cast<u32x4*>(sw + (buf * Epad + row) * RLD + c * 8) = rw[i];
-      }
-    }
-  };
-
-  const int fr = lane & 31;         // fragment row (expert or token within the tile)
-  const int fk = (lane >> 5) * 8;   // fragment k offset
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    if (step + 1 < nsteps) gload(step + 1);
-#pragma unroll
-    for (int k16 = 0; k16 < RBK / 16; ++k16) {
-      const bf16x8 bq0 = *reinterpret_cast<const bf16x8*>(sx + (buf * 64 + fr) * RLD + k16 * 16 + fk);
-      const bf16x8 bq1 = *reinterpret_cast<const bf16x8*>(sx + (buf * 64 + 32 + fr) * RLD + k16 * 16 + fk);
-#pragma unroll
-      for (int u = 0; u < MAXU; ++u) {
+      for (int u = 0; u < EW; ++u) {
         const int et = wave + 4 * u;
         if (et < n_et) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sw + (buf * Epad + et * 32 + fr) * RLD + k16 * 16 + fk);
-          acc[u][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq0, acc[u][0], 0, 0, 0);
-          acc[u][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq1, acc[u][1], 0, 0, 0);
+          const int row = et * 32 + fr;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+            acc[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[tt], acc[u][tt], 0, 0, 0);
         }
       }
     }
-    if (step + 1 < nsteps) sstore(buf ^ 1);
-    __syncthreads();
   }
+  __syncthreads();  // ring reads done before the logits tile overwrites it
 
   // D[i][j] of a 32x32 tile: lane holds column j = lane % 32 (token) and rows
   // i = 8*(r/4) + 4*(lane/32) + r%4 (experts) of accumulator element r.
+  float* lg = reinterpret_cast<float*>(smem);
   const int ld = Epad + 4;
 #pragma unroll
-  for (int u = 0; u < MAXU; ++u) {
+  for (int u = 0; u < EW; ++u) {
     const int et = wave + 4 * u;
     if (et < n_et) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int t = tt * 32 + fr;
-          const int e = et * 32 + 8 * g + 4 * (lane >> 5);
+          const int e = et * 32 + 8 * g + 4 * half;
           floatx4 v = {acc[u][tt][4 * g], acc[u][tt][4 * g + 1], acc[u][tt][4 * g + 2],
                        acc[u][tt][4 * g + 3]};
           *reinterpret_cast<floatx4*>(lg + t * ld + e) = v;
@@ -256,7 +318,8 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     }
   }
   __syncthreads();
-  topk_epilogue(lg, ld, tok0, ntok, E, k, bias, expert_idx, gate, hl, Epad, wave, lane);
+  topk_epilogue16<8 * EW>(lg, ld, TB, tok0, ntok, E, k, bias, expert_idx, gate, hl, Epad, wave,
+                          lane);
   __syncthreads();
   write_hist(hl, Epad, E, k, NB, b, hist, tid, 256);
 }
@@ -284,7 +347,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
   float* sx = reinterpret_cast<float*>(smem);  // [64][FBK+1]
   float* sw = sx + 64 * (FBK + 1);             // [Ecap][FBK+1]
   float* lg = reinterpret_cast<float*>(smem);  // [64][Ecap + 4]
-  const int64_t body = max(router_f32_stage_bytes(Ecap), router_lg_bytes(Ecap));
+  const int64_t body = max(router_f32_stage_bytes(Ecap), router_lg_bytes(64, Ecap));
   int* hl = reinterpret_cast<int*>(smem + body);
 
   for (int i = tid; i < k * Ecap; i += 256) hl[i] = 0;
@@ -388,24 +451,32 @@ hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, co
     if (err != hipSuccess) return err;
     const bf16_t* planes = reinterpret_cast<const bf16_t*>(ws_at(ws, p.off_planes));
     const int* flags = reinterpret_cast<const int*>(ws_at(ws, p.off_flags));
-    const int64_t lds = std::max(router_bf16_stage_bytes(p.Epad), router_lg_bytes(p.Epad)) +
-                        4LL * p.k * p.Epad;
     const bf16_t* xb = static_cast<const bf16_t*>(x);
-#define MOE_ROUTER_BF16(U)                                                                    \
-  do {                                                                                        \
-    if ((err = set_lds(router_bf16_kernel<U>, lds)) != hipSuccess) return err;                \
-    hipLaunchKernelGGL(router_bf16_kernel<U>, dim3(p.NB), dim3(256), lds, s, xb, planes, flags, \
-                       bias, T, d, p.E, p.Epad, p.k, expert_idx, gate, hist, p.NB);           \
+#define MOE_ROUTER_BF16(TT, EW, S)                                                               \
+  do {                                                                                           \
+    const int64_t lds = std::max(router_ring_bytes(p.Epad, 32 * TT, S),                          \
+                                 router_lg_bytes(32 * TT, p.Epad)) + 4LL * p.k * p.Epad;         \
+    if ((err = set_lds(router_bf16_kernel<TT, EW, S>, lds)) != hipSuccess) return err;           \
+    hipLaunchKernelGGL((router_bf16_kernel<TT, EW, S>), dim3(p.NB), dim3(256), lds, s, xb, planes, \
+                       flags, bias, T, d, p.E, p.Epad, p.k, expert_idx, gate, hist, p.NB);       \
   } while (0)
-    if (p.Epad <= 128) MOE_ROUTER_BF16(1);
-    else if (p.Epad <= 256) MOE_ROUTER_BF16(2);
-    else MOE_ROUTER_BF16(4);
+    if (p.Epad <= 128) {
+      if (p.TB == 32) MOE_ROUTER_BF16(1, 1, 4);
+      else if (p.TB == 64) MOE_ROUTER_BF16(2, 1, 4);
+      else MOE_ROUTER_BF16(4, 1, 4);
+    } else if (p.Epad <= 256) {
+      if (p.TB == 32) MOE_ROUTER_BF16(1, 2, 3);
+      else if (p.TB == 64) MOE_ROUTER_BF16(2, 2, 3);
+      else MOE_ROUTER_BF16(4, 2, 3);
+    } else {
+      MOE_ROUTER_BF16(1, 4, 2);
+    }
 #undef MOE_ROUTER_BF16
   } else {
     const float* xf = static_cast<const float*>(x);
 #define MOE_ROUTER_F32(N)                                                                        \
   do {                                                                                           \
-    const int64_t lds = std::max(router_f32_stage_bytes(4 * N), router_lg_bytes(4 * N)) +        \
+    const int64_t lds = std::max(router_f32_stage_bytes(4 * N), router_lg_bytes(64, 4 * N)) +        \
                         4LL * p.k * 4 * N;                                                       \
     if ((err = set_lds(router_f32_kernel<N>, lds)) != hipSuccess) return err;                    \
     hipLaunchKernelGGL(router_f32_kernel<N>, dim3(p.NB), dim3(256), lds, s, xf, w_r, bias, T, d, \
