@@ -263,34 +263,40 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
   cc = lc;
   int lk = 0;
   // Loads use a block-uniform per-expert base plus 32-bit lane offsets.
-  auto issue = [&](int slot) {
-    const int n0 = lc.nb * BN, m0 = lc.mb * BM;
+  // issue_one(slot, q) issues the q-th of the PER_STAGE direct-to-LDS
+  // instructions of the loader's current stage; advance() moves to the next.
+  auto issue_one = [&](int slot, int q) {
     unsigned char* base = smem + slot * STAGE;
-    const bf16_t* We = W + static_cast<int64_t>(lc.e) * N * K;
-    const bf16_t* Ae = A + static_cast<int64_t>(lc.e) * C * K;
-#pragma unroll
-    for (int q = 0; q < WL; ++q) {
+    if (q < WL) {
+      const bf16_t* We = W + static_cast<int64_t>(lc.e) * N * K;
       const int p = (wave * WL + q) * 64 + lane;
       const int row = p / CPR;
       const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
-      const uint32_t off = static_cast<uint32_t>(min(n0 + row, N - 1)) * K + lk * BK + c * 8;
+      const uint32_t off = static_cast<uint32_t>(min(lc.nb * BN + row, N - 1)) * K + lk * BK + c * 8;
       // non-temporal when each weight tile is read by one row block only
       __builtin_amdgcn_global_load_lds(We + off, (lds_void*)(base + (wave * WL + q) * 1024), 16, 0,
                                        NTW ? 2 : 0);
-    }
-    unsigned char* abase = base + BN * RB;
-#pragma unroll
-    for (int q = 0; q < AL; ++q) {
-      const int p = (wave * AL + q) * 64 + lane;
+    } else {
+      const int qa = q - WL;
+      const bf16_t* Ae = A + static_cast<int64_t>(lc.e) * C * K;
+      const int p = (wave * AL + qa) * 64 + lane;
       const int row = p / CPR;
       const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
-      const uint32_t off = static_cast<uint32_t>(min(m0 + row, lc.cnt - 1)) * K + lk * BK + c * 8;
-      __builtin_amdgcn_global_load_lds(Ae + off, (lds_void*)(abase + (wave * AL + q) * 1024), 16, 0, 0);
+      const uint32_t off = static_cast<uint32_t>(min(lc.mb * BM + row, lc.cnt - 1)) * K + lk * BK + c * 8;
+      __builtin_amdgcn_global_load_lds(Ae + off, (lds_void*)(base + BN * RB + (wave * AL + qa) * 1024),
+                                       16, 0, 0);
     }
+  };
+  auto advance = [&]() {
     if (++lk == KS) {
       lk = 0;
       next(lc);
     }
+  };
+  auto issue = [&](int slot) {
+#pragma unroll
+    for (int q = 0; q < PER_STAGE; ++q) issue_one(slot, q);
+    advance();
   };
 
   floatx16 acc[TN][TM];
@@ -312,7 +318,10 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
       if (total - 1 - s >= S - 2) wait_vmcnt<(S - 2) * PER_STAGE>();
       else wait_vmcnt<0>();
       ring_barrier();
-      if (s + S - 1 < total) issue((s + S - 1) % S);
+      // the next stage's loads are spread between this stage's MFMAs, so that
+      // issuing them does not stall the wave ahead of its math
+      const bool pf = s + S - 1 < total;
+      const int pslot = (s + S - 1) % S;
       const unsigned char* sw = smem + (s % S) * STAGE;
       const unsigned char* sa = sw + BN * RB;
       // fragments of sub-step j + 1 load while sub-step j's MFMAs run
@@ -330,7 +339,8 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
           fa[buf][i] = *reinterpret_cast<const bf16x8*>(sw + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
         }
       };
-      constexpr int NJ = BK / 16;  // MFMA sub-steps per stage
+      constexpr int NJ = BK / 16;           // MFMA sub-steps per stage
+      constexpr int MT = NJ * TN * TM;      // MFMAs per stage
       load_frags(0, 0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -338,10 +348,16 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < TN; ++i)
 #pragma unroll
-          for (int t = 0; t < TM; ++t)
+          for (int t = 0; t < TM; ++t) {
+            const int mi = (j * TN + i) * TM + t;
+#pragma unroll
+            for (int q = 0; q < PER_STAGE; ++q)
+              if (q * MT / PER_STAGE == mi && pf) issue_one(pslot, q);
             acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j & 1][i], fb[j & 1][t], acc[i][t], 0, 0, 0);
+          }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (pf) advance();
     }
     // tile done: D[n][m], lane holds m = lane % 32 and four consecutive n per group
     const int m0 = cc.mb * BM, n0 = cc.nb * BN;
