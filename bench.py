@@ -183,6 +183,10 @@ def main():
         "gemm_down": timed(lambda: moe.expert_down(cfg, hidden, cnt_t, w2, y_e, stream), R),
         "combine": timed(lambda: moe.combine(cfg, y_e, idx_t, slot_t, gate_t, y2, stream), R),
     }
+    try:  # the single-launch FFN, where its shape conditions hold
+        kern_us["ffn_fused"] = timed(lambda: moe.expert_ffn_fused(cfg, x_e, cnt_t, w1, w2, y_e, stream), R)
+    except moe.MoeError:
+        pass
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -198,6 +202,7 @@ def main():
                        + 8 * wl.T * wl.k, flops=2.0 * wl.T * d * wl.E if wl.route == "topk" else 0.0),
         "combine": dict(bytes=served * d * es + 12 * wl.T * wl.k + wl.T * d * es, flops=0.0),
         "dispatch": dict(bytes=wl.T * d * es + served * d * es + 8 * wl.T * wl.k, flops=0.0),
+        "ffn_fused": dict(bytes=2 * wbytes + 2 * served * d * es, flops=4.0 * served * d * f),
     }
     dom = max(("gemm_up", "gemm_down"), key=lambda n: kern_us[n])
     dom_us = kern_us[dom]

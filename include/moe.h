@@ -153,6 +153,18 @@ int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* expert_idx
 int moe_expert_ffn(const moe_config* cfg, const void* x_e, const int32_t* expert_count,
                    const void* w1, const void* w2, void* y_e, void* ws, void* stream);
 
+/* Step 4 in one launch, without the hidden activations in memory (bf16 only;
+ * capacity 1..64, d_model a multiple of 384, d_ff a multiple of 128; otherwise
+ * MOE_ERR_UNSUPPORTED).  Same arguments and results as moe_expert_ffn, bit for
+ * bit (each hidden and output element is accumulated from the same bf16
+ * products in the same order), and no workspace: per expert, d_ff is walked in
+ * chunks of 128 whose activated hidden tile stays in on-chip memory and is
+ * multiplied into register accumulators of y_e at once.  It moves no hidden
+ * bytes but streams w1 once per 384-column group of y_e; moe_expert_ffn is the
+ * faster choice on the Switch-Base shape (E=128, d_model=768, C=64). */
+int moe_expert_ffn_fused(const moe_config* cfg, const void* x_e, const int32_t* expert_count,
+                         const void* w1, const void* w2, void* y_e, void* stream);
+
 /* The two halves of step 4, for callers that keep the hidden activations:
  *   moe_expert_up:   hidden[e, s] = act(x_e[e, s] W1_e)   (one grouped GEMM launch)
  *   moe_expert_down: y_e[e, s]    = hidden[e, s] W2_e     (one grouped GEMM launch)

@@ -97,6 +97,12 @@ TEST_WORKLOADS = {
                                n_groups=4),
     "zipf_small_bf16": Workload("zipf_small_bf16", T=2048, d_model=256, d_ff=512, E=40, k=2,
                                 capacity_factor=1.25, act="gelu", dtype="bf16", zipf_s=1.1),
+    # d_model a multiple of 384 with capacity <= 64 (the single-pass expert FFN),
+    # top-1 with two 384-column groups per expert, and top-2 with one
+    "wide_top1_bf16": Workload("wide_top1_bf16", T=1500, d_model=768, d_ff=384, E=24, k=1,
+                               capacity_factor=1.0, act="gelu", dtype="bf16"),
+    "wide_top2_bf16": Workload("wide_top2_bf16", T=1200, d_model=384, d_ff=256, E=40, k=2,
+                               capacity_factor=1.0, act="relu", dtype="bf16"),
 }
 
 

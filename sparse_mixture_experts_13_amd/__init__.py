@@ -19,7 +19,7 @@ from ._lib import ACT, DTYPE, EXPORTS, REGION, ROUTE, MoeConfig, load  # noqa: F
 
 __all__ = ["MoeConfig", "MoeError", "make_config", "config_for", "capacity", "workspace_bytes",
            "workspace_offset", "alloc_workspace", "workspace_view", "router", "dispatch",
-           "expert_ffn", "expert_up", "expert_down", "combine", "forward", "version", "load"]
+           "expert_ffn", "expert_ffn_fused", "expert_up", "expert_down", "combine", "forward", "version", "load"]
 
 
 class MoeError(RuntimeError):
@@ -122,6 +122,11 @@ def dispatch(cfg, x, expert_idx, slot, expert_count, slot_token, x_e, ws, stream
 def expert_ffn(cfg, x_e, expert_count, w1, w2, y_e, ws, stream=None) -> None:
     _status(load().moe_expert_ffn(ctypes.byref(cfg), _ptr(x_e), _ptr(expert_count), _ptr(w1),
                                   _ptr(w2), _ptr(y_e), _ptr(ws), _stream(stream)))
+
+
+def expert_ffn_fused(cfg, x_e, expert_count, w1, w2, y_e, stream=None) -> None:
+    _status(load().moe_expert_ffn_fused(ctypes.byref(cfg), _ptr(x_e), _ptr(expert_count),
+                                        _ptr(w1), _ptr(w2), _ptr(y_e), _stream(stream)))
 
 
 def expert_up(cfg, x_e, expert_count, w1, hidden, stream=None) -> None:

@@ -15,7 +15,7 @@ REGION = {"expert_idx": 0, "gate": 1, "slot": 2, "expert_count": 3, "slot_token"
           "x_e": 5, "hidden": 6, "y_e": 7}
 
 EXPORTS = ["moe_capacity", "moe_workspace_bytes", "moe_workspace_offset", "moe_router",
-           "moe_dispatch", "moe_expert_ffn", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_last_error",
+           "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_fused", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_last_error",
            "moe_version"]
 
 
@@ -62,6 +62,8 @@ def load() -> ctypes.CDLL:
     lib.moe_dispatch.restype = ctypes.c_int
     lib.moe_expert_ffn.argtypes = [cfgp, P, P, P, P, P, P, P]
     lib.moe_expert_ffn.restype = ctypes.c_int
+    lib.moe_expert_ffn_fused.argtypes = [cfgp, P, P, P, P, P, P]
+    lib.moe_expert_ffn_fused.restype = ctypes.c_int
     lib.moe_expert_up.argtypes = [cfgp, P, P, P, P, P]
     lib.moe_expert_up.restype = ctypes.c_int
     lib.moe_expert_down.argtypes = [cfgp, P, P, P, P, P]

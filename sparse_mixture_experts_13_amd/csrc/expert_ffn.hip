@@ -386,6 +386,250 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused expert FFN for capacities <= 64, where one 64-row block holds every
+// token of an expert: y_e = act(x_e . w1[e]^T) . w2[e]^T with the hidden
+// activations kept on chip (the two-launch path writes and re-reads them, and
+// those writes, mixed into the weight stream, cost HBM read efficiency).
+//
+// Work items are (expert e, column group j of y_e) for the non-empty experts,
+// NO = 192 * NH columns per group, split evenly over persistent blocks of 8
+// waves; the items of one expert are consecutive, so they run on one XCD and
+// read w1[e] through one L2 (temporal loads), while each w2 row is read by one
+// item only (non-temporal).  An item walks d_ff in chunks of 128:
+//   * d_model / 64 up stages: 128 rows of w1 and the 64 activation rows, one
+//     64-k slice each; wave w accumulates the 32 x 32 hidden tile
+//     (f tile w % 4, row tile w / 4);
+//   * the chunk's hidden tile, activated and rounded to bf16, is written to
+//     LDS in the stage row layout (two 64-k slices of 64 rows);
+//   * 2 * NH down stages: 192 rows of w2 (column group hg of the item) for one
+//     64-k slice of the chunk; the four waves whose half matches hg % 2
+//     accumulate 3 output tiles each of that group, in registers across chunks.
+// Every stage is 192 rows of 128 bytes (three direct-to-LDS instructions per
+// wave), so the ring keeps one load count per stage.  Each hidden and output
+// element sees the same MFMA operands in the same k order as in the two-launch
+// path, so the results are identical to it.
+// ---------------------------------------------------------------------------
+constexpr int kFusedFC = 128;    // d_ff chunk per hidden tile
+constexpr int kFusedRows = 192;  // rows per stage: 128 of w1 + 64 activations, or 192 of w2
+
+template <int S>
+__host__ __device__ constexpr int ffn_fused_lds_bytes() {
+  return S * kFusedRows * 128 + 2 * 64 * 128 + (kMaxE + 1) * 4;
+}
+
+template <int ACT, int NH, int S>
+__global__ __launch_bounds__(512) void ffn_fused_bf16_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ W1, const bf16_t* __restrict__ W2,
+    bf16_t* __restrict__ out, const int32_t* __restrict__ count, int E, int64_t C, int d, int f,
+    int nspl) {
+  static_assert(NH % 2 == 0, "column groups alternate between the two wave halves");
+  constexpr int STAGE = kFusedRows * 128;
+  constexpr int PER = kFusedRows / 8 / 8;  // direct-to-LDS instructions per wave per stage
+  static_assert((S - 2) * PER < 64, "memory counter range");
+  constexpr int NO = NH * 192;             // y_e columns per item
+  constexpr int YG = NH / 2;               // column groups per wave
+  constexpr int KD = 2 * NH;               // down stages per chunk
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* hbuf = smem + S * STAGE;  // hidden tile: [2 slices][64 rows][128 bytes]
+  int* pre = reinterpret_cast<int*>(hbuf + 2 * 64 * 128);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, fr = lane & 31;
+  const int KU = d / 64;                   // up stages per chunk
+  const int SPC = KU + KD;                 // stages per chunk
+  const int NCH = f / kFusedFC;
+
+  auto rows_of = [&](int e) {
+    int64_t c = count[e];
+    return static_cast<int>(c < 0 ? 0 : (c > C ? C : c));
+  };
+  if (wave == 0) {
+    int run = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+      const int e = e0 + lane;
+      const int t = (e < E && rows_of(e) > 0) ? nspl : 0;
+      const int incl = wave_inclusive_scan(t, lane) + run;
+      if (e < E) pre[e + 1] = incl;
+      run = __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) pre[0] = 0;
+  }
+  __syncthreads();
+  const int V = pre[E];
+  const int G = gridDim.x;
+  const int g = xcd_major_id(blockIdx.x, G);
+  const int v0 = static_cast<int>(static_cast<int64_t>(g) * V / G);
+  const int v1 = static_cast<int>(static_cast<int64_t>(g + 1) * V / G);
+  const int total = (v1 - v0) * NCH * SPC;
+  if (total == 0) return;
+
+  struct Item { int v, e, j, cnt; };
+  auto seek = [&](Item& it, int v) {
+    it.v = v;
+    int e = 0;
+    while (pre[e + 1] <= v) ++e;
+    it.e = e;
+    it.j = v - pre[e];
+    it.cnt = rows_of(e);
+  };
+  auto next = [&](Item& it) {
+    ++it.v;
+    if (++it.j == nspl) {
+      it.j = 0;
+      do { ++it.e; } while (it.e < E && pre[it.e + 1] <= it.v);
+      if (it.e < E) it.cnt = rows_of(it.e);
+    }
+  };
+
+  // loader: item li, chunk lfc, stage lp inside the chunk
+  Item li;
+  seek(li, v0);
+  int lfc = 0, lp = 0;
+  auto issue = [&](int slot) {
+    unsigned char* base = smem + slot * STAGE;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int ii = wave * PER + q;           // 8 stage rows per instruction
+      const int row = ii * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ lds_swz_n<8>(row);
+      lds_void* dst = (lds_void*)(base + ii * 1024);
+      if (lp < KU) {
+        if (ii * 8 < kFusedFC) {
+          const bf16_t* w = W1 + static_cast<int64_t>(li.e) * f * d;
+          const uint32_t off = static_cast<uint32_t>(lfc * kFusedFC + row) * d + lp * 64 + c * 8;
+          __builtin_amdgcn_global_load_lds(w + off, dst, 16, 0, 0);
+        } else {
+          const bf16_t* a = A + static_cast<int64_t>(li.e) * C * d;
+          const uint32_t off = static_cast<uint32_t>(min(row - kFusedFC, li.cnt - 1)) * d + lp * 64 + c * 8;
+          __builtin_amdgcn_global_load_lds(a + off, dst, 16, 0, 0);
+        }
+      } else {
+        const int pd = lp - KU, kd = pd / NH, hg = pd - kd * NH;
+        const bf16_t* w = W2 + static_cast<int64_t>(li.e) * d * f;
+        const uint32_t off = static_cast<uint32_t>(li.j * NO + hg * 192 + row) * f +
+                             (lfc * 2 + kd) * 64 + c * 8;
+        __builtin_amdgcn_global_load_lds(w + off, dst, 16, 0, 2);
+      }
+    }
+    if (++lp == SPC) {
+      lp = 0;
+      if (++lfc == NCH) {
+        lfc = 0;
+        next(li);
+      }
+    }
+  };
+
+  floatx16 hacc;
+  floatx16 yacc[YG][3];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) hacc[r] = 0.f;
+#pragma unroll
+  for (int u = 0; u < YG; ++u)
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) yacc[u][i][r] = 0.f;
+
+  Item ci = li;
+  int cfc = 0, cp = 0;
+  const int uft = wave & 3, umt = wave >> 2;                // up: f tile, row tile
+  const int dgrp = wave >> 2, dmt = (wave >> 1) & 1, dnt = (wave & 1) * 3;  // down
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i)
+    if (i < total) issue(i);
+  for (int s = 0; s < total; ++s) {
+    if (total - 1 - s >= S - 2) wait_vmcnt<(S - 2) * PER>();
+    else wait_vmcnt<0>();
+    ring_barrier();
+    if (s + S - 1 < total) issue((s + S - 1) % S);
+    const unsigned char* sb = smem + (s % S) * STAGE;
+    if (cp < KU) {
+      // up: hidden[f][m] += w1 rows . activation rows over this 64-k slice
+      const int ra = uft * 32 + fr, rb = kFusedFC + umt * 32 + fr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 2 * j + half;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + ra * 128 + 16 * (c ^ lds_swz_n<8>(ra)));
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(sb + rb * 128 + 16 * (c ^ lds_swz_n<8>(rb)));
+        hacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, hacc, 0, 0, 0);
+      }
+      if (cp == KU - 1) {
+        // lane holds row m = umt*32 + fr and f = uft*32 + 8q + 4*half + r
+        const int m = umt * 32 + fr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int fl = uft * 32 + 8 * q;
+          const int c = (fl & 63) >> 3;
+          uint2 v;
+          v.x = pack_bf16x2(apply_act<ACT>(hacc[4 * q]), apply_act<ACT>(hacc[4 * q + 1]));
+          v.y = pack_bf16x2(apply_act<ACT>(hacc[4 * q + 2]), apply_act<ACT>(hacc[4 * q + 3]));
+          *reinterpret_cast<uint2*>(hbuf + (fl >> 6) * 8192 + m * 128 + 16 * (c ^ lds_swz_n<8>(m)) + 8 * half) = v;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hacc[r] = 0.f;
+      }
+    } else {
+      // down: y[n][m] += w2 rows (group hg) . hidden rows over slice kd of the chunk
+      const int pd = cp - KU, kd = pd / NH, hg = pd - kd * NH;
+      if ((hg & 1) == dgrp) {
+        const unsigned char* hb = hbuf + kd * 8192;
+        const int rb = dmt * 32 + fr;
+#pragma unroll
+        for (int u = 0; u < YG; ++u) {
+          if (2 * u + dgrp != hg) continue;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int c = 2 * j + half;
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(hb + rb * 128 + 16 * (c ^ lds_swz_n<8>(rb)));
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+              const int ra = (dnt + i) * 32 + fr;
+              const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + ra * 128 + 16 * (c ^ lds_swz_n<8>(ra)));
+              yacc[u][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, yacc[u][i], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if (cp == SPC - 1 && cfc == NCH - 1) {
+        // item done: lane holds row m and four consecutive columns per group
+        const int m = dmt * 32 + fr;
+        if (m < ci.cnt) {
+#pragma unroll
+          for (int u = 0; u < YG; ++u)
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+              const int n0 = ci.j * NO + (2 * u + dgrp) * 192 + (dnt + i) * 32 + 4 * half;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int n = n0 + 8 * q;
+                uint2 v;
+                v.x = pack_bf16x2(yacc[u][i][4 * q], yacc[u][i][4 * q + 1]);
+                v.y = pack_bf16x2(yacc[u][i][4 * q + 2], yacc[u][i][4 * q + 3]);
+                *reinterpret_cast<uint2*>(out + (static_cast<int64_t>(ci.e) * C + m) * d + n) = v;
+              }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < YG; ++u)
+#pragma unroll
+          for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) yacc[u][i][r] = 0.f;
+      }
+    }
+    if (++cp == SPC) {
+      cp = 0;
+      if (++cfc == NCH) {
+        cfc = 0;
+        next(ci);
+      }
+    }
+  }
+}
+
 // float32 grouped GEMM: 64 x 64 tile, 4 x 4 outputs per thread, BK = 16.
 template <int ACT>
 __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(const float* __restrict__ A,
@@ -485,6 +729,22 @@ static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
   return hipGetLastError();
 }
 
+template <int ACT, int NH, int S>
+static hipError_t run_fused(const Plan& p, int nspl, const bf16_t* A, const bf16_t* W1,
+                            const bf16_t* W2, bf16_t* out, const int32_t* count, hipStream_t s) {
+  auto kern = ffn_fused_bf16_kernel<ACT, NH, S>;
+  constexpr int lds = ffn_fused_lds_bytes<S>();
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err != hipSuccess) return err;
+  const int64_t items = static_cast<int64_t>(p.E) * nspl;
+  const int64_t grid = std::min<int64_t>(items, 256);  // one persistent block per CU
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), lds, s, A, W1, W2, out,
+                     count, p.E, p.C, static_cast<int>(p.d), static_cast<int>(p.f), nspl);
+  return hipGetLastError();
+}
+
 template <int ACT>
 static hipError_t run_f32(int E, const float* A, const float* W, float* out, const int32_t* count,
                           int64_t C, int N, int K, hipStream_t s) {
@@ -500,14 +760,42 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // Tile shapes by capacity.  Capacity <= 160: one row block holds every token of
 // an expert, so the GEMM is bound by streaming the weights once: persistent
 // direct-to-LDS ring kernel (8 or 4 waves, 256 weight rows per tile, 3-stage
-// ring).  Larger capacities: LDS-tiled 128 x 128 kernel.
+// ring).  When 384-row weight tiles cover N exactly and give at most one tile
+// per CU, a 4-wave 384-row tile with a 2-stage ring balances the CUs better
+// (every CU streams one tile) than 256-row tiles (one or two per CU).
+// Larger capacities: LDS-tiled 128 x 128 kernel.
 template <int ACT>
 static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf16_t* out,
                             const int32_t* count, int N, int K, hipStream_t s) {
+  if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
+    return run_ring<2, 3, 1, 4, 2, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 128) return run_ring<4, 1, 1, 8, 3, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 160) return run_ring<5, 2, 1, 4, 3, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
   return run_bf16<128, 128, 2, 2, ACT>(p.E, A, W, out, count, p.C, N, K, s);
+}
+
+// Column groups per expert for the fused FFN, or 0 where it does not apply:
+// bf16, capacity <= 64, d_ff a multiple of 128, and d_model a multiple of 384
+// split into column groups of 384 (NH = 2: 64 accumulator registers per lane;
+// wider groups spill).
+int fused_ffn_split(const Plan& p) {
+  if (p.dtype != 1 || p.C > 64 || p.C < 1 || p.f % kFusedFC != 0 || p.d % 384 != 0) return 0;
+  if (p.d * p.f >= (int64_t(1) << 31)) return 0;  // 32-bit offsets inside one expert
+  return static_cast<int>(p.d / 384);
+}
+
+hipError_t launch_expert_ffn_fused(const Plan& p, int nspl, const void* x_e,
+                                   const int32_t* expert_count, const void* w1, const void* w2,
+                                   void* y_e, hipStream_t s) {
+  if (p.C == 0) return hipSuccess;
+  const bf16_t* a = static_cast<const bf16_t*>(x_e);
+  const bf16_t* u = static_cast<const bf16_t*>(w1);
+  const bf16_t* v = static_cast<const bf16_t*>(w2);
+  bf16_t* o = static_cast<bf16_t*>(y_e);
+  if (p.d != static_cast<int64_t>(nspl) * 384) return hipErrorInvalidValue;
+  return p.act == 0 ? run_fused<0, 2, 5>(p, nspl, a, u, v, o, expert_count, s)
+                    : run_fused<1, 2, 5>(p, nspl, a, u, v, o, expert_count, s);
 }
 
 hipError_t launch_expert_up(const Plan& p, const void* x_e, const int32_t* expert_count,

@@ -253,6 +253,29 @@ int moe_expert_ffn(const moe_config* cfg, const void* x_e, const int32_t* expert
   return MOE_OK;
 }
 
+int moe_expert_ffn_fused(const moe_config* cfg, const void* x_e, const int32_t* expert_count,
+                         const void* w1, const void* w2, void* y_e, void* stream) {
+  MOE_CHECK(validate(cfg));
+  moe::Plan p;
+  make_plan(cfg, p);
+  const int nspl = moe::fused_ffn_split(p);
+  if (nspl == 0)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "fused expert FFN needs bf16, 1 <= capacity <= 64, d_model % 384 == 0 and "
+                "d_ff % 128 == 0");
+  const int64_t EC = int64_t(p.E) * p.C;
+  const int64_t wbytes = int64_t(p.E) * p.d * p.f * p.elem;
+  MOE_CHECK(need(x_e, EC * p.d * p.elem, "x_e"));
+  MOE_CHECK(need(expert_count, int64_t(p.E) * 4, "expert_count"));
+  MOE_CHECK(need(w1, wbytes, "w1"));
+  MOE_CHECK(need(w2, wbytes, "w2"));
+  MOE_CHECK(need(y_e, EC * p.d * p.elem, "y_e"));
+  MOE_HIP(moe::launch_expert_ffn_fused(p, nspl, x_e, expert_count, w1, w2, y_e,
+                                       static_cast<hipStream_t>(stream)),
+          "fused expert ffn");
+  return MOE_OK;
+}
+
 int moe_expert_up(const moe_config* cfg, const void* x_e, const int32_t* expert_count,
                   const void* w1, void* hidden, void* stream) {
   MOE_CHECK(validate(cfg));

@@ -44,6 +44,12 @@ hipError_t launch_expert_ffn(const Plan& p, const void* x_e, const int32_t* expe
                              const void* w1, const void* w2, void* y_e, void* ws, hipStream_t s);
 hipError_t launch_expert_up(const Plan& p, const void* x_e, const int32_t* expert_count,
                             const void* w1, void* hidden, hipStream_t s);
+// Fused FFN (bf16, capacity <= 64): column groups per expert, 0 if not applicable.
+int fused_ffn_split(const Plan& p);
+// y_e = act(x_e W1) W2 in one launch, the hidden activations kept on chip.
+hipError_t launch_expert_ffn_fused(const Plan& p, int nspl, const void* x_e,
+                                   const int32_t* expert_count, const void* w1, const void* w2,
+                                   void* y_e, hipStream_t s);
 hipError_t launch_expert_down(const Plan& p, const void* hidden, const int32_t* expert_count,
                               const void* w2, void* y_e, hipStream_t s);
 

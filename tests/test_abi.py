@@ -181,6 +181,31 @@ def test_null_and_misaligned_pointers_rejected():
     assert lib.moe_last_error().decode().startswith("group_id")
 
 
+@pytest.mark.parametrize("over,msg", [
+    (dict(dtype=0, d_model=384), "bf16"),                       # float32
+    (dict(d_model=320), "d_model % 384"),                       # 320 % 384 != 0
+    (dict(d_model=384, d_ff=192), "d_ff % 128"),                # 192 % 128 != 0
+    (dict(d_model=384, T=1000, E=8, k=1), "capacity <= 64"),    # C = 157
+])
+def test_fused_ffn_rejects_unsupported_shapes(over, msg):
+    lib = moe.load()
+    cfg = _cfg(**over)
+    ok = ctypes.c_void_p(0x100000)
+    rc = lib.moe_expert_ffn_fused(ctypes.byref(cfg), ok, ok, ok, ok, ok, None)
+    assert rc == _lib.MOE_ERR_UNSUPPORTED
+    assert msg in lib.moe_last_error().decode()
+
+
+def test_fused_ffn_checks_pointers():
+    lib = moe.load()
+    cfg = _cfg(d_model=384, d_ff=256)
+    ok = ctypes.c_void_p(0x100000)
+    assert lib.moe_expert_ffn_fused(ctypes.byref(cfg), ok, ok, ok, ok, None, None) == _lib.MOE_ERR_ARG
+    assert lib.moe_last_error().decode().startswith("y_e")
+    assert lib.moe_expert_ffn_fused(ctypes.byref(cfg), ok, ok, None, ok, ok, None) == _lib.MOE_ERR_ARG
+    assert lib.moe_last_error().decode().startswith("w1")
+
+
 def test_binding_raises_on_error():
     cfg = moe.make_config(10, 64, 64, 4, 5, 1.0)
     with pytest.raises(moe.MoeError, match="k must be"):

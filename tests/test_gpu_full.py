@@ -51,3 +51,24 @@ def test_full_size_forward(name):
     err = check_layer_output(wl, y_got, y_ref, served, name)
     drops = int((ref["slot"] < 0).sum())
     print(f"[gpu] full {name}: ok, y err {err:.3g}, drops {drops}, {time.time() - t0:.1f}s", flush=True)
+
+
+def test_full_size_fused_ffn_switch_base():
+    """moe_expert_ffn_fused on the Switch-Base shape equals moe_expert_ffn bit for bit."""
+    import torch
+    import sparse_mixture_experts_13_amd as moe
+    from gpu_util import raw_bits
+    wl = W.WORKLOADS["switch_base_bf16"]
+    print("[gpu] full fused ffn switch_base_bf16", flush=True)
+    inputs = W.make_inputs(wl, with_weights=False)
+    dev = Dev(wl, inputs)
+    dev.upload_weights_per_expert()
+    steps = dev.run_steps()
+    y_e = torch.zeros_like(steps["y_e"])
+    moe.expert_ffn_fused(dev.cfg, steps["x_e"], steps["expert_count"], dev.w1, dev.w2, y_e)
+    torch.cuda.synchronize()
+    counts = steps["expert_count"].cpu().numpy()
+    a, b = raw_bits(steps["y_e"]), raw_bits(y_e)
+    for e in range(wl.E):
+        n = int(counts[e])
+        np.testing.assert_array_equal(b[e, :n], a[e, :n], err_msg=f"fused y_e expert {e}")

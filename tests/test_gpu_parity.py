@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import moe_workloads as W
+import sparse_mixture_experts_13_amd as moe
 import oracle
 from gpu_util import (Dev, check_layer_output, check_routing, max_abs_rel, out_tol, raw_bits,
                       to_dev, to_host_f64)
@@ -73,6 +74,28 @@ def test_forward_matches_oracle_and_steps(name):
     assert torch.equal(fw["y"], steps["y"]), "forward and step-wise results differ"
 
 
+FUSED = ["wide_top1_bf16", "wide_top2_bf16", "rre_small_bf16"]
+
+
+@pytest.mark.parametrize("name", FUSED)
+def test_fused_ffn_matches_two_launch_ffn(name):
+    """moe_expert_ffn_fused: bit-identical to moe_expert_ffn, and within tolerance of the oracle."""
+    wl = W.TEST_WORKLOADS[name]
+    print(f"[gpu] fused ffn {name}", flush=True)
+    inputs = W.make_inputs(wl)
+    ref = _oracle(wl, inputs)
+    dev = Dev(wl, inputs)
+    steps = dev.run_steps()
+    y_e = torch.zeros_like(steps["y_e"])
+    moe.expert_ffn_fused(dev.cfg, steps["x_e"], steps["expert_count"], dev.w1, dev.w2, y_e)
+    torch.cuda.synchronize()
+    ye, ye2 = raw_bits(steps["y_e"]), raw_bits(y_e)
+    for e in range(wl.E):
+        n = int(ref["expert_count"][e])
+        np.testing.assert_array_equal(ye2[e, :n], ye[e, :n], err_msg=f"fused y_e expert {e}")
+    _check_y_e(wl, y_e, ref)
+
+
 @pytest.mark.parametrize("name", ["switch_small_bf16", "xmoe_small_bf16", "tiny_switch_f32"])
 def test_combine_alone(name):
     """Combine on oracle-provided expert outputs (rounded to the storage dtype)."""
@@ -93,7 +116,6 @@ def test_combine_alone(name):
     y_ref = oracle.combine([ye_val[e] for e in range(wl.E)], ref["expert_idx"], ref["slot"],
                            ref["gate"], wl.d_model)
     y = torch.empty((wl.T, wl.d_model), dtype=dev.x.dtype, device="cuda")
-    import sparse_mixture_experts_13_amd as moe
     moe.combine(dev.cfg, to_dev(ye_store), to_dev(ref["expert_idx"]), to_dev(ref["slot"]),
                 to_dev(ref["gate"]), y)
     torch.cuda.synchronize()
