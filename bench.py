@@ -183,6 +183,10 @@ def main():
         "gemm_down": timed(lambda: moe.expert_down(cfg, hidden, cnt_t, w2, y_e, stream), R),
         "combine": timed(lambda: moe.combine(cfg, y_e, idx_t, slot_t, gate_t, y2, stream), R),
     }
+    if wl.route == "topk":  # router + load-balancing loss (Eq. 4-6)
+        aux_t = torch.empty(1 + 2 * wl.E, dtype=torch.float32, device=dev)
+        kern_us["router_aux"] = timed(
+            lambda: moe.router_aux(cfg, x, w_r, bias, idx2, gate2, 1e-2, aux_t, ws, stream), R)
     try:  # the single-launch FFN, where its shape conditions hold
         kern_us["ffn_fused"] = timed(lambda: moe.expert_ffn_fused(cfg, x_e, cnt_t, w1, w2, y_e, stream), R)
     except moe.MoeError:

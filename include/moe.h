@@ -124,6 +124,22 @@ int moe_router(const moe_config* cfg, const void* x, const float* w_r, const flo
                const int32_t* group_id, int32_t* expert_idx, float* gate, void* ws,
                void* stream);
 
+/* Step 1 plus the load-balancing auxiliary loss of Switch notes 2.2 (Eq. 4-6),
+ * learned routing only (RRE has no router probabilities: MOE_ERR_UNSUPPORTED).
+ * Arguments and results of moe_router, and
+ *   alpha  the loss coefficient (Switch uses 1e-2)
+ *   aux    [1 + 2E] float32 out: aux[0] = alpha * E * sum_i f_i * P_i,
+ *          aux[1 + i] = f_i, the fraction of the T tokens whose first choice
+ *          (the argmax of the router probability, equal logits to the lower
+ *          index) is expert i, before any capacity drop (Eq. 5);
+ *          aux[1 + E + i] = P_i, the mean over the T tokens of the router
+ *          probability of expert i (Eq. 6).
+ * P_i sums float32 probabilities per router block in a fixed order and the
+ * blocks in float64, so repeated calls give identical bits.  T must be >= 1. */
+int moe_router_aux(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
+                   int32_t* expert_idx, float* gate, double alpha, float* aux, void* ws,
+                   void* stream);
+
 /* Steps 2 and 3, capacity-limited dispatch and gather.  Switch notes 2.2
  * (Eq. 3 capacity; an assignment to a full expert is dropped).
  * Assignments are placed choice by choice and, inside a choice, in token

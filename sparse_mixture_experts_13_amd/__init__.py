@@ -18,7 +18,7 @@ from typing import Optional
 from ._lib import ACT, DTYPE, EXPORTS, REGION, ROUTE, MoeConfig, load  # noqa: F401
 
 __all__ = ["MoeConfig", "MoeError", "make_config", "config_for", "capacity", "workspace_bytes",
-           "workspace_offset", "alloc_workspace", "workspace_view", "router", "dispatch",
+           "workspace_offset", "alloc_workspace", "workspace_view", "router", "router_aux", "dispatch",
            "expert_ffn", "expert_ffn_fused", "expert_up", "expert_down", "combine", "forward", "version", "load"]
 
 
@@ -111,6 +111,12 @@ def workspace_view(ws, cfg: MoeConfig, region: str):
 def router(cfg, x, w_r, bias, group_id, expert_idx, gate, ws, stream=None) -> None:
     _status(load().moe_router(ctypes.byref(cfg), _ptr(x), _ptr(w_r), _ptr(bias), _ptr(group_id),
                               _ptr(expert_idx), _ptr(gate), _ptr(ws), _stream(stream)))
+
+
+def router_aux(cfg, x, w_r, bias, expert_idx, gate, alpha, aux, ws, stream=None) -> None:
+    _status(load().moe_router_aux(ctypes.byref(cfg), _ptr(x), _ptr(w_r), _ptr(bias),
+                                  _ptr(expert_idx), _ptr(gate), float(alpha), _ptr(aux), _ptr(ws),
+                                  _stream(stream)))
 
 
 def dispatch(cfg, x, expert_idx, slot, expert_count, slot_token, x_e, ws, stream=None) -> None:

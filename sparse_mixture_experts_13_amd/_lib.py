@@ -14,7 +14,7 @@ ROUTE = {"topk": 0, "rre": 1}
 REGION = {"expert_idx": 0, "gate": 1, "slot": 2, "expert_count": 3, "slot_token": 4,
           "x_e": 5, "hidden": 6, "y_e": 7}
 
-EXPORTS = ["moe_capacity", "moe_workspace_bytes", "moe_workspace_offset", "moe_router",
+EXPORTS = ["moe_capacity", "moe_workspace_bytes", "moe_workspace_offset", "moe_router", "moe_router_aux",
            "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_fused", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_last_error",
            "moe_version"]
 
@@ -58,6 +58,8 @@ def load() -> ctypes.CDLL:
     lib.moe_workspace_offset.restype = i64
     lib.moe_router.argtypes = [cfgp, P, P, P, P, P, P, P, P]
     lib.moe_router.restype = ctypes.c_int
+    lib.moe_router_aux.argtypes = [cfgp, P, P, P, P, P, ctypes.c_double, P, P, P]
+    lib.moe_router_aux.restype = ctypes.c_int
     lib.moe_dispatch.argtypes = [cfgp, P, P, P, P, P, P, P, P]
     lib.moe_dispatch.restype = ctypes.c_int
     lib.moe_expert_ffn.argtypes = [cfgp, P, P, P, P, P, P, P]

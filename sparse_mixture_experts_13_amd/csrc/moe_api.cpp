@@ -123,6 +123,8 @@ void make_plan(const moe_config* cfg, moe::Plan& p) {
   off = align_up(off + 3LL * p.Epad * p.d * 2);
   p.off_flags = off;
   off = align_up(off + moe::kSplitBlocks * 4);
+  p.off_psum = off;  // per router block: probability sum of every expert (float)
+  off = align_up(off + int64_t(p.NB) * p.Epad * 4);
   p.total = off;
 }
 
@@ -211,6 +213,24 @@ int moe_router(const moe_config* cfg, const void* x, const float* w_r, const flo
   make_plan(cfg, p);
   MOE_CHECK(check_router_args(p, x, w_r, group_id, expert_idx, gate, ws));
   return run_router(p, x, w_r, bias, group_id, expert_idx, gate, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_router_aux(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
+                   int32_t* expert_idx, float* gate, double alpha, float* aux, void* ws,
+                   void* stream) {
+  MOE_CHECK(validate(cfg));
+  if (cfg->route != MOE_ROUTE_TOPK)
+    return fail(MOE_ERR_UNSUPPORTED, "the load-balancing loss needs learned (top-k) routing");
+  if (!std::isfinite(alpha)) return fail(MOE_ERR_ARG, "alpha must be finite");
+  moe::Plan p;
+  make_plan(cfg, p);
+  MOE_CHECK(check_router_args(p, x, w_r, nullptr, expert_idx, gate, ws));
+  MOE_CHECK(need(aux, (1 + 2 * int64_t(p.E)) * 4, "aux"));
+  if (p.T == 0) return fail(MOE_ERR_ARG, "the load-balancing loss needs T >= 1");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_HIP(moe::launch_router_topk(p, x, w_r, bias, expert_idx, gate, ws, s, true), "router");
+  MOE_HIP(moe::launch_router_aux(p, alpha, aux, ws, s), "load-balancing loss");
+  return MOE_OK;
 }
 
 int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* expert_idx, int32_t* slot,

@@ -21,13 +21,17 @@ struct Plan {
   int elem;                // bytes per element of dtype
   // workspace byte offsets
   int64_t off_region[8];
-  int64_t off_hist, off_offsets, off_planes, off_flags, total;
+  int64_t off_hist, off_offsets, off_planes, off_flags, off_psum, total;
 };
 
 // router.hip
 hipError_t launch_router_split(const Plan& p, const float* w_r, void* ws, hipStream_t s);
+// with_psum: also write the per-block expert probability sums (load-balancing loss)
 hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, const float* bias,
-                              int32_t* expert_idx, float* gate, void* ws, hipStream_t s);
+                              int32_t* expert_idx, float* gate, void* ws, hipStream_t s,
+                              bool with_psum = false);
+// aux = [alpha * E * sum_i f_i P_i, f[E], P[E]] from the router's block rows
+hipError_t launch_router_aux(const Plan& p, double alpha, float* aux, void* ws, hipStream_t s);
 hipError_t launch_router_rre(const Plan& p, const int32_t* group_id, int32_t* expert_idx,
                              float* gate, void* ws, hipStream_t s);
 

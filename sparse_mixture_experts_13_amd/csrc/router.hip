@@ -18,6 +18,12 @@
 // lanes rank each token with 64-bit keys (logit, then lower index).  The block's
 // expert histogram is built in LDS for the dispatch scan.  float32 tokens use a
 // float32 FMA kernel with the same ranking, 64 tokens per block.
+//
+// Load-balancing loss (Switch notes 2.2, Eq. 4-6), on request: the epilogue
+// also adds up every expert's softmax probability over the block's tokens, in
+// a fixed order (lane, then the token groups of a wave, then the waves), into
+// one row per router block; a one-block kernel adds the rows in block order
+// (float64) for P_i and takes f_i from the first-choice histogram.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -45,10 +51,16 @@ __device__ __forceinline__ int key_expert(uint64_t key) {
 
 // Rank the tokens of one block.  lg: logits [64][ld] in LDS (bias not yet added).
 // Wave w handles tokens w, w+4, ...; lane l holds experts l, l+64, ...
+// psum (may be null): the block's row of per-expert probability sums; red:
+// [4][ldh] floats of LDS for the cross-wave sum, free once ranking is done.
 __device__ void topk_epilogue(const float* lg, int ld, int tok0, int ntok, int E, int k,
                               const float* __restrict__ bias, int32_t* __restrict__ expert_idx,
-                              float* __restrict__ gate, int* hl, int ldh, int wave, int lane) {
+                              float* __restrict__ gate, int* hl, int ldh, int wave, int lane,
+                              float* __restrict__ psum, float* red) {
   const int nper = (E + kWave - 1) / kWave;  // <= 8
+  float pacc[kMaxE / kWave];
+#pragma unroll
+  for (int i = 0; i < kMaxE / kWave; ++i) pacc[i] = 0.f;
   for (int t = wave; t < ntok; t += 4) {
     const float* row = lg + t * ld;
     float hv[kMaxE / kWave];
@@ -90,6 +102,21 @@ __device__ void topk_epilogue(const float* lg, int ld, int tok0, int ntok, int E
       gate[o] = p;
       atomicAdd(&hl[lane * ldh + e], 1);
     }
+    if (psum) {
+#pragma unroll
+      for (int i = 0; i < kMaxE / kWave; ++i) pacc[i] += expf(hv[i] - hmax) / s;
+    }
+  }
+  if (psum) {
+    __syncthreads();  // every wave is done with the logits tile that red overlays
+#pragma unroll
+    for (int i = 0; i < kMaxE / kWave; ++i) {
+      const int e = lane + kWave * i;
+      if (i < nper && e < ldh) red[wave * ldh + e] = pacc[i];
+    }
+    __syncthreads();
+    for (int e = wave * kWave + lane; e < E; e += 4 * kWave)
+      psum[e] = ((red[e] + red[ldh + e]) + red[2 * ldh + e]) + red[3 * ldh + e];
   }
 }
 
@@ -154,8 +181,12 @@ __host__ __device__ inline int64_t router_lg_bytes(int TB, int Epad) {
 template <int NV>
 __device__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int ntok, int E, int k,
                                 const float* __restrict__ bias, int32_t* __restrict__ expert_idx,
-                                float* __restrict__ gate, int* hl, int ldh, int wave, int lane) {
+                                float* __restrict__ gate, int* hl, int ldh, int wave, int lane,
+                                float* __restrict__ psum, float* red) {
   const int grp = lane >> 4, sub = lane & 15;
+  float pacc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) pacc[i] = 0.f;
   for (int base = 0; base < TB; base += 16) {
     const int t = base + wave * 4 + grp;
     const bool valid = t < ntok;
@@ -203,6 +234,29 @@ __device__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int n
       gate[o] = expf(key_logit(mine) - hmax) / sum;
       atomicAdd(&hl[sub * ldh + e], 1);
     }
+    if (psum && valid) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) pacc[i] += expf(hv[i] - hmax) / sum;  // 0 past E
+    }
+  }
+  if (psum) {
+    // the wave's four token groups: (g0 + g1) + (g2 + g3), the same on every lane
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      pacc[i] += __shfl_xor(pacc[i], 16, kWave);
+      pacc[i] += __shfl_xor(pacc[i], 32, kWave);
+    }
+    __syncthreads();  // every wave is done with the logits tile that red overlays
+    if (grp == 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = sub + 16 * i;
+        if (e < ldh) red[wave * ldh + e] = pacc[i];
+      }
+    }
+    __syncthreads();
+    for (int e = wave * kWave + lane; e < E; e += 4 * kWave)
+      psum[e] = ((red[e] + red[ldh + e]) + red[2 * ldh + e]) + red[3 * ldh + e];
   }
 }
 
@@ -210,7 +264,8 @@ template <int TT, int EW, int S>
 __global__ __launch_bounds__(256) void router_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, const int* __restrict__ flags,
     const float* __restrict__ bias, int T, int d, int E, int Epad, int k,
-    int32_t* __restrict__ expert_idx, float* __restrict__ gate, int* __restrict__ hist, int NB) {
+    int32_t* __restrict__ expert_idx, float* __restrict__ gate, int* __restrict__ hist, int NB,
+    float* __restrict__ psum) {
   constexpr int TB = 32 * TT;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -319,7 +374,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   }
   __syncthreads();
   topk_epilogue16<8 * EW>(lg, ld, TB, tok0, ntok, E, k, bias, expert_idx, gate, hl, Epad, wave,
-                          lane);
+                          lane, psum ? psum + static_cast<int64_t>(b) * Epad : nullptr, lg);
   __syncthreads();
   write_hist(hl, Epad, E, k, NB, b, hist, tid, 256);
 }
@@ -337,7 +392,7 @@ template <int NACC>
 __global__ __launch_bounds__(256) void router_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ expert_idx, float* __restrict__ gate,
-    int* __restrict__ hist, int NB) {
+    int* __restrict__ hist, int NB, float* __restrict__ psum, int ldp) {
   constexpr int Ecap = 4 * NACC;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -378,7 +433,8 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 #pragma unroll
   for (int j = 0; j < NACC; ++j) lg[t * ld + eg + 4 * j] = acc[j];
   __syncthreads();
-  topk_epilogue(lg, ld, tok0, ntok, E, k, bias, expert_idx, gate, hl, Ecap, wave, lane);
+  topk_epilogue(lg, ld, tok0, ntok, E, k, bias, expert_idx, gate, hl, Ecap, wave, lane,
+                psum ? psum + static_cast<int64_t>(b) * ldp : nullptr, lg);
   __syncthreads();
   write_hist(hl, Ecap, E, k, NB, b, hist, tid, 256);
 }
@@ -424,6 +480,41 @@ __global__ __launch_bounds__(64) void router_rre_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Load-balancing loss from the per-block rows: P_i = (sum over blocks of the
+// probability sums) / T, f_i = (first choices of expert i) / T, loss =
+// alpha * E * sum_i f_i P_i (float64 sums in a fixed order).
+// aux = [loss, f_0 .. f_{E-1}, P_0 .. P_{E-1}].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_aux_kernel(const float* __restrict__ psum, int ldp,
+                                                         const int* __restrict__ hist, int T,
+                                                         int E, int k, int NB, double alpha,
+                                                         float* __restrict__ aux) {
+  __shared__ double part[256];
+  const int tid = threadIdx.x;
+  double acc = 0.0;
+  for (int e = tid; e < E; e += 256) {
+    double P = 0.0;
+    int64_t cnt = 0;
+    for (int b = 0; b < NB; ++b) {
+      P += static_cast<double>(psum[static_cast<int64_t>(b) * ldp + e]);
+      cnt += hist[(static_cast<int64_t>(e) * k) * NB + b];
+    }
+    P /= T;
+    const double f = static_cast<double>(cnt) / T;
+    aux[1 + e] = static_cast<float>(f);
+    aux[1 + E + e] = static_cast<float>(P);
+    acc += f * P;
+  }
+  part[tid] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) part[tid] += part[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) aux[0] = static_cast<float>(alpha * E * part[0]);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_router_split(const Plan& p, const float* w_r, void* ws, hipStream_t s) {
@@ -441,9 +532,11 @@ static hipError_t set_lds(K kernel, int64_t bytes) {
 }
 
 hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, const float* bias,
-                              int32_t* expert_idx, float* gate, void* ws, hipStream_t s) {
+                              int32_t* expert_idx, float* gate, void* ws, hipStream_t s,
+                              bool with_psum) {
   if (p.T == 0) return hipSuccess;
   int* hist = reinterpret_cast<int*>(ws_at(ws, p.off_hist));
+  float* psum = with_psum ? reinterpret_cast<float*>(ws_at(ws, p.off_psum)) : nullptr;
   const int T = static_cast<int>(p.T), d = static_cast<int>(p.d);
   hipError_t err;
   if (p.dtype == 1) {
@@ -458,7 +551,7 @@ hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, co
                                  router_lg_bytes(32 * TT, p.Epad)) + 4LL * p.k * p.Epad;         \
     if ((err = set_lds(router_bf16_kernel<TT, EW, S>, lds)) != hipSuccess) return err;           \
     hipLaunchKernelGGL((router_bf16_kernel<TT, EW, S>), dim3(p.NB), dim3(256), lds, s, xb, planes, \
-                       flags, bias, T, d, p.E, p.Epad, p.k, expert_idx, gate, hist, p.NB);       \
+                       flags, bias, T, d, p.E, p.Epad, p.k, expert_idx, gate, hist, p.NB, psum); \
   } while (0)
     if (p.Epad <= 128) {
       if (p.TB == 32) MOE_ROUTER_BF16(1, 1, 4);
@@ -480,7 +573,7 @@ hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, co
                         4LL * p.k * 4 * N;                                                       \
     if ((err = set_lds(router_f32_kernel<N>, lds)) != hipSuccess) return err;                    \
     hipLaunchKernelGGL(router_f32_kernel<N>, dim3(p.NB), dim3(256), lds, s, xf, w_r, bias, T, d, \
-                       p.E, p.k, expert_idx, gate, hist, p.NB);                                  \
+                       p.E, p.k, expert_idx, gate, hist, p.NB, psum, p.Epad);                   \
   } while (0)
     if (p.E <= 32) MOE_ROUTER_F32(8);
     else if (p.E <= 64) MOE_ROUTER_F32(16);
@@ -489,6 +582,14 @@ hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, co
     else MOE_ROUTER_F32(128);
 #undef MOE_ROUTER_F32
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_aux(const Plan& p, double alpha, float* aux, void* ws, hipStream_t s) {
+  const float* psum = reinterpret_cast<const float*>(ws_at(ws, p.off_psum));
+  const int* hist = reinterpret_cast<const int*>(ws_at(ws, p.off_hist));
+  hipLaunchKernelGGL(router_aux_kernel, dim3(1), dim3(256), 0, s, psum, p.Epad, hist,
+                     static_cast<int>(p.T), p.E, p.k, p.NB, alpha, aux);
   return hipGetLastError();
 }
 

@@ -119,6 +119,16 @@ class Dev:
         torch.cuda.synchronize()
         return r
 
+    def run_router_aux(self, alpha=1e-2):
+        """moe_router_aux: routing plus [loss, f[E], P[E]]."""
+        wl = self.wl
+        idx = self.new((wl.T, wl.k), torch.int32)
+        gate = self.new((wl.T, wl.k), torch.float32)
+        aux = self.new((1 + 2 * wl.E,), torch.float32)
+        moe.router_aux(self.cfg, self.x, self.w_r, self.bias, idx, gate, alpha, aux, self.ws)
+        torch.cuda.synchronize()
+        return idx, gate, aux.cpu().numpy()
+
     def run_forward(self):
         wl = self.wl
         y = self.new((wl.T, wl.d_model), elem_dtype(wl))
@@ -128,6 +138,32 @@ class Dev:
         for reg in ("expert_idx", "gate", "slot", "expert_count", "slot_token"):
             out[reg] = moe.workspace_view(self.ws, self.cfg, reg)
         return out
+
+
+def aux_tol(E: int) -> float:
+    """Relative bound on P_i and the loss: a float32 probability (exp, a sum over
+    the E experts, a division) summed over at most 128 tokens of a router block
+    in float32, the blocks in float64: (E + 2 * 128 + 64) units of 2^-24."""
+    return (E + 320) * 2.0 ** -24
+
+
+def check_router_aux(wl, inputs, idx, gate, aux, alpha=1e-2, label=""):
+    """Loss, f and P of moe_router_aux against the oracle's Eq. 4-6 on the same logits."""
+    import oracle
+    h = oracle.router_logits(inputs["x"], inputs["w_r"], inputs["bias"])
+    E, T = wl.E, wl.T
+    top1 = oracle.topk(h, 1)[:, 0]
+    f_ref = np.bincount(top1, minlength=E) / T
+    P_ref = oracle.softmax(h).mean(axis=0)
+    loss_ref = oracle.aux_loss(h, alpha=alpha)
+    np.testing.assert_array_equal(idx[:, 0].cpu().numpy(), top1, err_msg=f"{label} first choice")
+    np.testing.assert_array_equal(aux[1:1 + E], f_ref.astype(np.float32), err_msg=f"{label} f")
+    P = aux[1 + E:].astype(np.float64)
+    rel = np.abs(P - P_ref) / np.maximum(P_ref, 1e-300)
+    assert rel.max() <= aux_tol(E), f"{label} P rel err {rel.max():.3g} > {aux_tol(E):.3g}"
+    err = abs(float(aux[0]) - loss_ref) / loss_ref
+    assert err <= aux_tol(E), f"{label} loss rel err {err:.3g} (gpu {aux[0]}, oracle {loss_ref})"
+    return err
 
 
 def check_routing(wl, got, ref, label=""):

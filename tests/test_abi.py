@@ -206,6 +206,25 @@ def test_fused_ffn_checks_pointers():
     assert lib.moe_last_error().decode().startswith("w1")
 
 
+def test_router_aux_rejections():
+    lib = moe.load()
+    ok = ctypes.c_void_p(0x100000)
+    rre = _cfg(route=1, k=1, n_groups=4)
+    assert lib.moe_router_aux(ctypes.byref(rre), ok, ok, None, ok, ok, 0.01, ok, ok, None) == \
+        _lib.MOE_ERR_UNSUPPORTED
+    assert "top-k" in lib.moe_last_error().decode()
+    cfg = _cfg()
+    assert lib.moe_router_aux(ctypes.byref(cfg), ok, ok, None, ok, ok, 0.01, None, ok, None) == \
+        _lib.MOE_ERR_ARG
+    assert lib.moe_last_error().decode().startswith("aux")
+    assert lib.moe_router_aux(ctypes.byref(cfg), ok, ok, None, ok, ok, float("nan"), ok, ok, None) == \
+        _lib.MOE_ERR_ARG
+    assert "alpha" in lib.moe_last_error().decode()
+    empty = _cfg(T=0)
+    assert lib.moe_router_aux(ctypes.byref(empty), ok, ok, None, ok, ok, 0.01, ok, ok, None) == \
+        _lib.MOE_ERR_ARG
+
+
 def test_binding_raises_on_error():
     cfg = moe.make_config(10, 64, 64, 4, 5, 1.0)
     with pytest.raises(moe.MoeError, match="k must be"):

@@ -13,7 +13,7 @@ import pytest
 
 import moe_workloads as W
 import oracle
-from gpu_util import Dev, check_layer_output, check_routing, to_host_f64
+from gpu_util import Dev, check_layer_output, check_router_aux, check_routing, to_host_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -72,3 +72,15 @@ def test_full_size_fused_ffn_switch_base():
     for e in range(wl.E):
         n = int(counts[e])
         np.testing.assert_array_equal(b[e, :n], a[e, :n], err_msg=f"fused y_e expert {e}")
+
+
+@pytest.mark.parametrize("name", ["switch_base_bf16", "large_zipf_top2_bf16"])
+def test_full_size_router_aux(name):
+    """moe_router_aux at full size: Eq. 4-6 against the oracle on the same logits."""
+    wl = W.WORKLOADS[name]
+    print(f"[gpu] full router aux {name}", flush=True)
+    inputs = W.make_inputs(wl, with_weights=False)
+    dev = Dev(wl, inputs)
+    idx, gate, aux = dev.run_router_aux(alpha=1e-2)
+    err = check_router_aux(wl, inputs, idx, gate, aux, 1e-2, name)
+    print(f"[gpu] full router aux {name}: loss {aux[0]:.6g}, rel err {err:.3g}", flush=True)

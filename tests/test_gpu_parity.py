@@ -13,8 +13,8 @@ import torch
 import moe_workloads as W
 import sparse_mixture_experts_13_amd as moe
 import oracle
-from gpu_util import (Dev, check_layer_output, check_routing, max_abs_rel, out_tol, raw_bits,
-                      to_dev, to_host_f64)
+from gpu_util import (Dev, check_layer_output, check_router_aux, check_routing, max_abs_rel,
+                      out_tol, raw_bits, to_dev, to_host_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,6 +94,41 @@ def test_fused_ffn_matches_two_launch_ffn(name):
         n = int(ref["expert_count"][e])
         np.testing.assert_array_equal(ye2[e, :n], ye[e, :n], err_msg=f"fused y_e expert {e}")
     _check_y_e(wl, y_e, ref)
+
+
+AUX = [n for n in SMALL if W.TEST_WORKLOADS[n].route == "topk"]
+
+
+@pytest.mark.parametrize("name", AUX)
+def test_router_aux_loss(name):
+    """moe_router_aux: the routing of moe_router, and Eq. 4-6 against the oracle."""
+    wl = W.TEST_WORKLOADS[name]
+    print(f"[gpu] router aux {name}", flush=True)
+    inputs = W.make_inputs(wl, with_weights=False)
+    dev = Dev(wl, inputs)
+    idx, gate, aux = dev.run_router_aux(alpha=1e-2)
+    idx0 = torch.empty_like(idx)
+    gate0 = torch.empty_like(gate)
+    moe.router(dev.cfg, dev.x, dev.w_r, dev.bias, None, idx0, gate0, dev.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx0) and torch.equal(gate, gate0), "router_aux routing differs from router"
+    check_router_aux(wl, inputs, idx, gate, aux, 1e-2, name)
+    _, _, aux2 = dev.run_router_aux(alpha=1e-2)
+    np.testing.assert_array_equal(aux, aux2)   # fixed summation order: identical bits
+
+
+def test_router_aux_uniform_routing_gives_alpha():
+    """Eq. 4 closed form: all-equal logits route every token to expert 0 (f_0 = 1)
+    with P_i = 1/E for every i, so the loss is alpha * E * (1/E) = alpha."""
+    wl = W.TEST_WORKLOADS["switch_small_bf16"].replace(T=333)
+    inputs = W.make_inputs(wl, with_weights=False)
+    inputs["w_r"] = np.zeros_like(inputs["w_r"])
+    dev = Dev(wl, inputs)
+    idx, _, aux = dev.run_router_aux(alpha=0.25)
+    assert (idx[:, 0].cpu().numpy() == 0).all()
+    assert aux[1] == 1.0 and (aux[2:1 + wl.E] == 0).all()
+    np.testing.assert_allclose(aux[1 + wl.E:], 1.0 / wl.E, rtol=2 ** -20)
+    assert abs(float(aux[0]) - 0.25) <= 0.25 * 2 ** -20
 
 
 @pytest.mark.parametrize("name", ["switch_small_bf16", "xmoe_small_bf16", "tiny_switch_f32"])
