@@ -763,10 +763,15 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // ring).  When 384-row weight tiles cover N exactly and give at most one tile
 // per CU, a 4-wave 384-row tile with a 2-stage ring balances the CUs better
 // (every CU streams one tile) than 256-row tiles (one or two per CU).
-// Larger capacities: LDS-tiled 128 x 128 kernel.
+// Capacity > 384: the same persistent ring with 256 x 256 tiles (8 waves of
+// 4 x 2 MFMA tiles, 2-stage ring of 64 KB stages; each weight tile is read by
+// every 256-row block of its expert, so those loads stay temporal).  Capacity
+// 161..384: the LDS-tiled 128 x 128 kernel, which wastes less on a partly
+// filled last row block (measured at capacity 320).
 template <int ACT>
 static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf16_t* out,
                             const int32_t* count, int N, int K, hipStream_t s) {
+  if (p.C > 384) return run_ring<4, 2, 2, 4, 2, 64, false, ACT>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
     return run_ring<2, 3, 1, 4, 2, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);

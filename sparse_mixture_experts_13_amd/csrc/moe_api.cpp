@@ -123,8 +123,8 @@ void make_plan(const moe_config* cfg, moe::Plan& p) {
   off = align_up(off + 3LL * p.Epad * p.d * 2);
   p.off_flags = off;
   off = align_up(off + moe::kSplitBlocks * 4);
-  p.off_psum = off;  // per router block: probability sum of every expert (float)
-  off = align_up(off + int64_t(p.NB) * p.Epad * 4);
+  p.off_psum = off;  // load-balancing loss: probability sums per router block, range sums
+  off = align_up(off + moe::aux_region_bytes(p));
   p.total = off;
 }
 

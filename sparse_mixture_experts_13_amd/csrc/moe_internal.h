@@ -32,6 +32,11 @@ hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, co
                               bool with_psum = false);
 // aux = [alpha * E * sum_i f_i P_i, f[E], P[E]] from the router's block rows
 hipError_t launch_router_aux(const Plan& p, double alpha, float* aux, void* ws, hipStream_t s);
+// Load-balancing workspace: per router block a float row of Epad probability
+// sums, then kAuxSplit rows of float64 sums and kAuxSplit rows of int64 counts.
+constexpr int kAuxSplit = 64;
+inline int64_t aux_rows_bytes(const Plan& p) { return (int64_t(p.NB) * p.Epad * 4 + 255) / 256 * 256; }
+inline int64_t aux_region_bytes(const Plan& p) { return aux_rows_bytes(p) + int64_t(kAuxSplit) * p.Epad * 16; }
 hipError_t launch_router_rre(const Plan& p, const int32_t* group_id, int32_t* expert_idx,
                              float* gate, void* ws, hipStream_t s);
 

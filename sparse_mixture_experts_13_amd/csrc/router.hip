@@ -482,22 +482,64 @@ __global__ __launch_bounds__(64) void router_rre_kernel(const int32_t* __restric
 // ---------------------------------------------------------------------------
 // Load-balancing loss from the per-block rows: P_i = (sum over blocks of the
 // probability sums) / T, f_i = (first choices of expert i) / T, loss =
-// alpha * E * sum_i f_i P_i (float64 sums in a fixed order).
+// alpha * E * sum_i f_i P_i.  Two launches, float64 sums in a fixed order:
+//   1. block (x, y): 64 experts x one of kAuxSplit contiguous ranges of router
+//      blocks, summed in block order -> part_p[y][e], part_c[y][e];
+//   2. one block: the ranges in order, then the loss over the experts.
 // aux = [loss, f_0 .. f_{E-1}, P_0 .. P_{E-1}].
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void router_aux_kernel(const float* __restrict__ psum, int ldp,
-                                                         const int* __restrict__ hist, int T,
-                                                         int E, int k, int NB, double alpha,
-                                                         float* __restrict__ aux) {
+__global__ __launch_bounds__(64) void router_aux_partial_kernel(
+    const float* __restrict__ psum, int ldp, const int* __restrict__ hist, int E, int k, int NB,
+    double* __restrict__ part_p, int64_t* __restrict__ part_c) {
+  const int e = blockIdx.x * 64 + threadIdx.x;
+  const int y = blockIdx.y, S = gridDim.y;
+  if (e >= E) return;
+  const int b0 = static_cast<int>(static_cast<int64_t>(y) * NB / S);
+  const int b1 = static_cast<int>(static_cast<int64_t>(y + 1) * NB / S);
+  double P = 0.0;
+  int64_t cnt = 0;
+  // sixteen loads in flight, then added in block order
+  for (int b = b0; b < b1; b += 16) {
+    float v[16];
+    int c[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      v[j] = b + j < b1 ? psum[static_cast<int64_t>(b + j) * ldp + e] : 0.f;
+      c[j] = b + j < b1 ? hist[(static_cast<int64_t>(e) * k) * NB + b + j] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      P += static_cast<double>(v[j]);
+      cnt += c[j];
+    }
+  }
+  part_p[static_cast<int64_t>(y) * ldp + e] = P;
+  part_c[static_cast<int64_t>(y) * ldp + e] = cnt;
+}
+
+__global__ __launch_bounds__(256) void router_aux_kernel(const double* __restrict__ part_p,
+                                                         const int64_t* __restrict__ part_c,
+                                                         int ldp, int S, int T, int E,
+                                                         double alpha, float* __restrict__ aux) {
   __shared__ double part[256];
   const int tid = threadIdx.x;
   double acc = 0.0;
   for (int e = tid; e < E; e += 256) {
     double P = 0.0;
     int64_t cnt = 0;
-    for (int b = 0; b < NB; ++b) {
-      P += static_cast<double>(psum[static_cast<int64_t>(b) * ldp + e]);
-      cnt += hist[(static_cast<int64_t>(e) * k) * NB + b];
+    for (int y = 0; y < S; y += 16) {
+      double v[16];
+      int64_t c[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        v[j] = y + j < S ? part_p[static_cast<int64_t>(y + j) * ldp + e] : 0.0;
+        c[j] = y + j < S ? part_c[static_cast<int64_t>(y + j) * ldp + e] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        P += v[j];
+        cnt += c[j];
+      }
     }
     P /= T;
     const double f = static_cast<double>(cnt) / T;
@@ -588,8 +630,14 @@ hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, co
 hipError_t launch_router_aux(const Plan& p, double alpha, float* aux, void* ws, hipStream_t s) {
   const float* psum = reinterpret_cast<const float*>(ws_at(ws, p.off_psum));
   const int* hist = reinterpret_cast<const int*>(ws_at(ws, p.off_hist));
-  hipLaunchKernelGGL(router_aux_kernel, dim3(1), dim3(256), 0, s, psum, p.Epad, hist,
-                     static_cast<int>(p.T), p.E, p.k, p.NB, alpha, aux);
+  // the range partials follow the block rows in the same region
+  double* part_p = reinterpret_cast<double*>(ws_at(ws, p.off_psum + aux_rows_bytes(p)));
+  int64_t* part_c = reinterpret_cast<int64_t*>(part_p + static_cast<int64_t>(kAuxSplit) * p.Epad);
+  const int S = std::min(kAuxSplit, p.NB);
+  hipLaunchKernelGGL(router_aux_partial_kernel, dim3((p.E + 63) / 64, S), dim3(64), 0, s, psum,
+                     p.Epad, hist, p.E, p.k, p.NB, part_p, part_c);
+  hipLaunchKernelGGL(router_aux_kernel, dim3(1), dim3(256), 0, s, part_p, part_c, p.Epad, S,
+                     static_cast<int>(p.T), p.E, alpha, aux);
   return hipGetLastError();
 }
 

@@ -222,6 +222,15 @@ def test_capacity_one():
     assert (ref["expert_count"] <= 1).all()
 
 
+@pytest.mark.parametrize("cf,kernel", [(3.2, "LDS-tiled 128x128"), (1.0, "ring, 64-row blocks")])
+def test_capacity_kernel_ranges(cf, kernel):
+    """Capacities that select the other grouped-GEMM kernels: 161..384 (C = 200 here)
+    and the smallest (C = 63)."""
+    wl = W.TEST_WORKLOADS["switch_small_bf16"].replace(capacity_factor=cf)
+    inputs = W.make_inputs(wl)
+    ref, _ = _run_case(wl, inputs, f"C={oracle.capacity(wl.T, wl.E, wl.k, cf)} {kernel}")
+
+
 def test_one_expert_takes_all():
     wl = BASE.replace(T=500, E=16, k=2, capacity_factor=1.25)
     inputs = W.make_inputs(wl)
