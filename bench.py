@@ -216,7 +216,8 @@ def main():
         bound, achieved, peak, unit = "mfma", algo[dom]["flops"] / dom_us / 1e6, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
         bound, achieved, peak, unit = "hbm", algo[dom]["bytes"] / dom_us / 1e3, HBM_PEAK_GBS, "GB/s"
-    kname = {"gemm_up": "ffn_gemm_bf16_kernel (up, act)", "gemm_down": "ffn_gemm_bf16_kernel (down)"}[dom]
+    kname = {"gemm_up": "grouped GEMM up-projection + act (moe_expert_up)",
+             "gemm_down": "grouped GEMM down-projection (moe_expert_down)"}[dom]
     traffic = read_traffic(dom, wl.name)
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kname,
