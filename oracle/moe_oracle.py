@@ -1,4 +1,4 @@
-"""CPU oracle of the sparse Mixture-of-Experts layer forward pass.
+"""CPU oracle of the sparse Mixture-of-Experts layer: forward pass, and its backward pass.
 
 TEST INFRASTRUCTURE. This module is the slow, obviously-correct reference the
 GPU library is checked against.  Only the tests, the package smoke check and the
@@ -371,3 +371,99 @@ def aux_loss(logits: np.ndarray, alpha: float = 1e-2) -> float:
     f = np.bincount(top1, minlength=N) / T
     P = softmax(logits).mean(axis=0)
     return float(alpha * N * np.sum(f * P))
+
+
+# ---------------------------------------------------------------------------
+# NEXT: backward pass of the layer
+# ---------------------------------------------------------------------------
+
+
+def act_grad(z: np.ndarray, act: str) -> np.ndarray:
+    """Derivative of ``act_fn``: ReLU 1 where z > 0 and 0 elsewhere (the value at the kink
+    z = 0 is taken as 0); GELU d/dz [z Phi(z)] = Phi(z) + z phi(z) with the standard normal
+    density phi(z) = exp(-z^2 / 2) / sqrt(2 pi)."""
+    if act == "relu":
+        return (z > 0.0).astype(np.float64)
+    if act == "gelu":
+        cdf = 0.5 * (1.0 + erf(z / math.sqrt(2.0)))
+        pdf = np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+        return cdf + z * pdf
+    raise ValueError(act)
+
+
+def served_choice(fwd: dict, e: int, s: int) -> tuple:
+    """(token, choice) that holds slot s of expert e."""
+    t = int(fwd["slot_token"][e, s])
+    for c in range(fwd["expert_idx"].shape[1]):
+        if int(fwd["expert_idx"][t, c]) == e and int(fwd["slot"][t, c]) == s:
+            return t, c
+    raise AssertionError("slot map inconsistent")
+
+
+def backward(wl, inputs, fwd: dict, dy: np.ndarray,
+             weights: Optional[Callable[[int], tuple]] = None) -> dict:
+    """Gradients of the layer for an upstream gradient dy = dL/dy [T, d_model] (float64).
+
+    The layer is [Switch] 2.1 Eq. 2, y(x) = sum over the served choices c of
+    p_{i_c}(x) E_{i_c}(x), with p = softmax(h) (Eq. 1), h = W_r x (+ bias) and
+    E_i(x) = act(x W1_i) W2_i; the gate keeps the router differentiable (2.1).
+    The chosen set and the capacity drop ([Switch] 2.2) are piecewise constant in
+    the inputs, so no gradient flows through them: this is the derivative
+    wherever they do not switch, and a dropped choice contributes nothing.
+    Per served choice (token t, choice c, expert e, slot s):
+      expert term: dE = p_e dy[t]; with Z = x W1_e, H = act(Z), E = H W2_e:
+        dW2_e += dE^T H, dH = dE W2_e^T, dZ = dH * act'(Z),
+        dW1_e += dZ^T x, dx[t] += dZ W1_e^T;
+      gate term: dp_e(t) = dy[t] . E_e(x_t), and through the softmax Jacobian
+        dh = p * (dp - <p, dp>), then dx[t] += dh W_r, dW_r += dh^T x, dbias += dh.
+    Random routed experts have constant gates 1: no router gradient (dw_r, dbias None).
+    Weights are taken at their stored values (``weights(e)`` -> (w1_e, w2_e) in the
+    stored [d_ff, d_model] / [d_model, d_ff] layout), every product in float64.
+    Returns dx [T, d], dw1 [E, f, d], dw2 [E, d, f], dw_r [E, d] or None,
+    dbias [E] or None, dgate [T, k] (dL/dp of each served choice, 0 if dropped).
+    """
+    if weights is None:
+        w1, w2 = inputs["w1"], inputs["w2"]
+        weights = lambda e: (w1[e], w2[e])  # noqa: E731
+    dy = np.asarray(dy, np.float64)
+    T, d, f, E, k = wl.T, wl.d_model, wl.d_ff, wl.E, wl.k
+    x = as_f64(inputs["x"])
+    dx = np.zeros((T, d))
+    dw1 = np.zeros((E, f, d))
+    dw2 = np.zeros((E, d, f))
+    dgate = np.zeros((T, k))
+    topk_route = wl.route == "topk"
+    p = softmax(fwd["logits"]) if topk_route else None
+    for e in range(E):
+        n = int(fwd["expert_count"][e])
+        if n == 0:
+            continue
+        w1_e, w2_e = (as_f64(w) for w in weights(e))
+        owners = [served_choice(fwd, e, s) for s in range(n)]
+        xe = x[[t for t, _ in owners]]
+        z = xe @ w1_e.T
+        hdn = act_fn(z, wl.act)
+        ye = hdn @ w2_e.T
+        g = np.array([p[t, e] if topk_route else 1.0 for t, _ in owners])
+        dye = g[:, None] * dy[[t for t, _ in owners]]
+        for s, (t, c) in enumerate(owners):
+            dgate[t, c] = float(dy[t] @ ye[s])
+        dw2[e] = dye.T @ hdn
+        dz = (dye @ w2_e) * act_grad(z, wl.act)
+        dw1[e] = dz.T @ xe
+        dxe = dz @ w1_e
+        for s, (t, _) in enumerate(owners):
+            dx[t] += dxe[s]
+    dw_r = dbias = None
+    if topk_route:
+        dp = np.zeros((T, E))
+        for t in range(T):
+            for c in range(k):
+                if int(fwd["slot"][t, c]) >= 0:
+                    dp[t, int(fwd["expert_idx"][t, c])] += dgate[t, c]
+        dh = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+        w_r = as_f64(inputs["w_r"])
+        dx += dh @ w_r
+        dw_r = dh.T @ x
+        dbias = dh.sum(axis=0) if inputs.get("bias") is not None else None
+    return dict(dx=dx, dw1=dw1, dw2=dw2, dw_r=dw_r, dbias=dbias, dgate=dgate)

@@ -412,3 +412,146 @@ def check_aux_loss(rng):
     # all tokens to expert 1 with p_1 = 3/4: f = (0, 1), P = (1/4, 3/4) -> 2 * 3/4 = 1.5
     lg3 = np.array([[0.0, math.log(3.0)]] * 3)
     assert abs(O.aux_loss(lg3, alpha=1.0) - 1.5) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+
+
+def _torch_dense_grads(wl, inp, r, dy):
+    """Gradients of <y, dy> by torch autograd (float64) on a dense formulation: every
+    expert on every token, y = sum_e m[t, e] softmax(h)[t, e] FFN_e(x_t), with m the
+    served-choice mask from the oracle's dispatch held constant."""
+    import torch
+    T, E = wl.T, wl.E
+    m = np.zeros((T, E))
+    for t in range(T):
+        for c in range(wl.k):
+            if r["slot"][t, c] >= 0:
+                m[t, r["expert_idx"][t, c]] = 1.0
+    x = torch.tensor(O.as_f64(inp["x"]), requires_grad=True)
+    w_r = torch.tensor(O.as_f64(inp["w_r"]), requires_grad=True)
+    w1 = torch.tensor(O.as_f64(inp["w1"]), requires_grad=True)
+    w2 = torch.tensor(O.as_f64(inp["w2"]), requires_grad=True)
+    h = x @ w_r.T
+    bias = None
+    if inp.get("bias") is not None:
+        bias = torch.tensor(O.as_f64(inp["bias"]), requires_grad=True)
+        h = h + bias
+    p = torch.softmax(h, dim=1)
+    act = torch.relu if wl.act == "relu" else (lambda z: torch.nn.functional.gelu(z, approximate="none"))
+    y = torch.zeros(T, wl.d_model, dtype=torch.float64)
+    mt = torch.tensor(m)
+    for e in range(E):
+        fe = act(x @ w1[e].T) @ w2[e].T
+        y = y + (mt[:, e] * p[:, e])[:, None] * fe
+    (y * torch.tensor(dy)).sum().backward()
+    out = dict(dx=x.grad.numpy(), dw_r=w_r.grad.numpy(), dw1=w1.grad.numpy(), dw2=w2.grad.numpy())
+    out["dbias"] = bias.grad.numpy() if bias is not None else None
+    return out
+
+
+def check_backward_autograd(rng):
+    # dyadic x and w_r: the float32 logits the oracle routes on equal the float64 ones;
+    # the tiny bias only breaks ties (rounded to float32 once, like the oracle's)
+    for (T, d, f, E, k, cf, act, zipf) in [(40, 16, 24, 4, 1, 1.0, "gelu", False),
+                                           (60, 8, 12, 6, 2, 1.0, "gelu", False),
+                                           (50, 16, 8, 5, 2, 0.5, "relu", True),
+                                           (24, 8, 8, 3, 3, 2.0, "gelu", False)]:
+        wl, inp = _rand_layer(rng, T, d, f, E, k, cf, act, zipf)
+        if not zipf:
+            inp["bias"] = None
+            inp["x"] = inp["x"] + (rng.integers(0, 64, size=inp["x"].shape) / 512).astype(np.float32)
+        r = O.forward(wl, inp)
+        dy = rng.normal(size=(T, d))
+        g = O.backward(wl, inp, r, dy)
+        ref = _torch_dense_grads(wl, inp, r, dy)
+        for key in ("dx", "dw_r", "dw1", "dw2"):
+            scale = max(np.abs(ref[key]).max(), 1e-300)
+            np.testing.assert_allclose(g[key] / scale, ref[key] / scale, atol=1e-6 if zipf else 1e-12,
+                                       err_msg=key)
+        if zipf:
+            scale = np.abs(ref["dbias"]).max()
+            np.testing.assert_allclose(g["dbias"] / scale, ref["dbias"] / scale, atol=1e-6)
+
+
+def check_backward_finite_differences(rng):
+    # central differences of L = <y, dy> in the expert weights (GELU: smooth; the
+    # routing does not depend on w1, w2).  The router weight is pinned by autograd
+    # instead: the forward stores float32 gates, whose rounding swamps a small step.
+    T, d, f, E, k = 30, 8, 10, 3, 2
+    wl, inp = _rand_layer(rng, T, d, f, E, k, 1.0, "gelu")
+    inp["bias"] = None
+    for key in ("w1", "w2"):
+        inp[key] = inp[key].astype(np.float64)
+    r = O.forward(wl, inp)
+    dy = rng.normal(size=(T, d))
+    g = O.backward(wl, inp, r, dy)
+
+    def loss(i2):
+        return float((O.forward(wl, i2)["y"] * dy).sum())
+
+    for key, grad in (("w1", g["dw1"]), ("w2", g["dw2"])):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in inp[key].shape)
+            eps = 1e-5
+            ip, im = dict(inp), dict(inp)
+            ip[key] = inp[key].copy(); ip[key][idx] += eps
+            im[key] = inp[key].copy(); im[key][idx] -= eps
+            fd = (loss(ip) - loss(im)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (key, idx, fd, grad[idx])
+
+
+def check_backward_single_expert_is_mlp(rng):
+    # E = 1, k = 1, no drops: gate 1 (softmax of one logit), the layer is a 2-layer MLP;
+    # torch.nn.Linear autograd gives dx, dW1, dW2, and the router gets no gradient
+    import torch
+    T, d, f = 30, 12, 20
+    for act in ("relu", "gelu"):
+        wl, inp = _rand_layer(rng, T, d, f, 1, 1, 1.0, act, ties=True)
+        inp["bias"] = None
+        r = O.forward(wl, inp)
+        dy = rng.normal(size=(T, d))
+        g = O.backward(wl, inp, r, dy)
+        xt = torch.tensor(inp["x"], dtype=torch.float64, requires_grad=True)
+        l1 = torch.nn.Linear(d, f, bias=False, dtype=torch.float64)
+        l2 = torch.nn.Linear(f, d, bias=False, dtype=torch.float64)
+        with torch.no_grad():
+            l1.weight.copy_(torch.tensor(inp["w1"][0], dtype=torch.float64))
+            l2.weight.copy_(torch.tensor(inp["w2"][0], dtype=torch.float64))
+        a = torch.relu if act == "relu" else (lambda z: torch.nn.functional.gelu(z, approximate="none"))
+        (l2(a(l1(xt))) * torch.tensor(dy)).sum().backward()
+        np.testing.assert_allclose(g["dx"], xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(g["dw1"][0], l1.weight.grad.numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(g["dw2"][0], l2.weight.grad.numpy(), rtol=1e-12, atol=1e-12)
+        assert np.abs(g["dw_r"]).max() == 0.0
+
+
+def check_backward_rre_no_router_grad(rng):
+    # random routed experts: gates are the constant 1, so dx is the expert path only and
+    # equals the sum of the per-expert MLP input gradients of the tokens each expert serves
+    T, d, f, E, G = 48, 8, 12, 8, 2
+    wl = _WL(T=T, d_model=d, d_ff=f, E=E, k=1, capacity_factor=2.0, act="gelu", route="rre",
+             n_groups=G)
+    x = (rng.integers(-8, 9, size=(T, d)) / 8).astype(np.float32)
+    w1 = (rng.normal(size=(E, f, d)) / math.sqrt(d)).astype(np.float32)
+    w2 = (rng.normal(size=(E, d, f)) / math.sqrt(f)).astype(np.float32)
+    inp = {"x": x, "w_r": None, "bias": None, "group_id": rng.integers(0, G, size=T).astype(np.int32),
+           "w1": w1, "w2": w2}
+    r = O.forward(wl, inp)
+    dy = rng.normal(size=(T, d))
+    g = O.backward(wl, inp, r, dy)
+    assert g["dw_r"] is None and g["dbias"] is None
+    import torch
+    dx_ref = np.zeros((T, d))
+    for t in range(T):
+        e, s = int(r["expert_idx"][t, 0]), int(r["slot"][t, 0])
+        if s < 0:
+            continue
+        xt = torch.tensor(O.as_f64(x[t:t + 1]), requires_grad=True)
+        z = xt @ torch.tensor(O.as_f64(w1[e])).T
+        yv = torch.nn.functional.gelu(z, approximate="none") @ torch.tensor(O.as_f64(w2[e])).T
+        (yv * torch.tensor(dy[t:t + 1])).sum().backward()
+        dx_ref[t] = xt.grad.numpy()[0]
+    np.testing.assert_allclose(g["dx"], dx_ref, rtol=1e-12, atol=1e-12)

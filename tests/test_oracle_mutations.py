@@ -117,6 +117,64 @@ def _rre_shifted(group_id, E, n_groups, seed):
     return idx, np.ones((T, 1), np.float32)
 
 
+def _gelu_grad_no_density(z, act):
+    if act == "gelu":
+        return 0.5 * (1.0 + np.vectorize(math.erf)(z / math.sqrt(2.0)))
+    return _orig["act_grad"](z, act)
+
+
+def _backward_variant(mode):
+    """The oracle backward with one planted mistake (test code only)."""
+    def bwd(wl, inputs, fwd, dy, weights=None):
+        if weights is None:
+            w1, w2 = inputs["w1"], inputs["w2"]
+            weights = lambda e: (w1[e], w2[e])  # noqa: E731
+        dy = np.asarray(dy, np.float64)
+        T, d, f, E, k = wl.T, wl.d_model, wl.d_ff, wl.E, wl.k
+        x = O.as_f64(inputs["x"])
+        dx, dw1, dw2, dgate = np.zeros((T, d)), np.zeros((E, f, d)), np.zeros((E, d, f)), np.zeros((T, k))
+        topk_route = wl.route == "topk"
+        p = O.softmax(fwd["logits"]) if topk_route else None
+        for e in range(E):
+            n = int(fwd["expert_count"][e])
+            if n == 0:
+                continue
+            w1_e, w2_e = (O.as_f64(w) for w in weights(e))
+            owners = [O.served_choice(fwd, e, s) for s in range(n)]
+            xe = x[[t for t, _ in owners]]
+            z = xe @ w1_e.T
+            hdn = O.act_fn(z, wl.act)
+            ye = hdn @ w2_e.T
+            g = np.array([p[t, e] if topk_route else 1.0 for t, _ in owners])
+            dye = dy[[t for t, _ in owners]] if mode == "no_gate" else g[:, None] * dy[[t for t, _ in owners]]
+            for s, (t, c) in enumerate(owners):
+                dgate[t, c] = float(dy[t] @ ye[s])
+            dw2[e] = dye.T @ hdn
+            dz = (dye @ w2_e) * O.act_grad(z, wl.act)
+            dw1[e] = (xe.T @ dz).T if mode != "dw1_from_hidden" else dz.T @ np.tile(xe, (1, 1))[:, :d] * 0.5
+            for s, (t, _) in enumerate(owners):
+                dx[t] += (dz @ w1_e)[s]
+        dw_r = dbias = None
+        if topk_route:
+            dp = np.zeros((T, E))
+            for t in range(T):
+                for c in range(k):
+                    if int(fwd["slot"][t, c]) >= 0:
+                        dp[t, int(fwd["expert_idx"][t, c])] += dgate[t, c]
+            if mode == "jacobian_sign":
+                dh = p * (np.sum(p * dp, axis=1, keepdims=True) - dp)
+            elif mode == "jacobian_diag_only":
+                dh = p * dp
+            else:
+                dh = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            w_r = O.as_f64(inputs["w_r"])
+            dx += dh @ w_r
+            dw_r = dh.T @ x
+            dbias = dh.sum(axis=0) if inputs.get("bias") is not None else None
+        return dict(dx=dx, dw1=dw1, dw2=dw2, dw_r=dw_r, dbias=dbias, dgate=dgate)
+    return bwd
+
+
 ALL_PINS = [
     lambda rng: P.check_worked_fixture("switch_top1_worked.json"),
     lambda rng: P.check_worked_fixture("top2_priority_worked.json"),
@@ -126,6 +184,8 @@ ALL_PINS = [
     P.check_dispatch_invariants, P.check_dispatch_no_drop, P.check_choice_priority,
     lambda rng: P.check_gelu_values(), P.check_dense_equals_sparse, P.check_single_expert_is_mlp,
     P.check_k_equals_E_is_softmax_mixture, P.check_expert_permutation, P.check_aux_loss,
+    P.check_backward_autograd, P.check_backward_finite_differences,
+    P.check_backward_single_expert_is_mlp, P.check_backward_rre_no_router_grad,
 ]
 
 MUTATIONS = {
@@ -145,6 +205,11 @@ MUTATIONS = {
     "w2_not_transposed": ("expert_apply", _expert_apply_w2_untransposed),
     "splitmix_wrong_shift": ("splitmix64", _splitmix_bad_shift),
     "rre_off_by_one_token": ("route_rre", _rre_shifted),
+    "gelu_grad_without_density_term": ("act_grad", _gelu_grad_no_density),
+    "backward_without_gate": ("backward", _backward_variant("no_gate")),
+    "backward_softmax_jacobian_sign": ("backward", _backward_variant("jacobian_sign")),
+    "backward_softmax_jacobian_diagonal": ("backward", _backward_variant("jacobian_diag_only")),
+    "backward_dw1_wrong": ("backward", _backward_variant("dw1_from_hidden")),
 }
 
 

@@ -86,3 +86,19 @@ def test_expert_permutation(rng):
 
 def test_aux_loss(rng):
     P.check_aux_loss(rng)
+
+
+def test_backward_autograd(rng):
+    P.check_backward_autograd(rng)
+
+
+def test_backward_finite_differences(rng):
+    P.check_backward_finite_differences(rng)
+
+
+def test_backward_single_expert_is_mlp(rng):
+    P.check_backward_single_expert_is_mlp(rng)
+
+
+def test_backward_rre(rng):
+    P.check_backward_rre_no_router_grad(rng)
