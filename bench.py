@@ -187,6 +187,17 @@ def main():
         aux_t = torch.empty(1 + 2 * wl.E, dtype=torch.float32, device=dev)
         kern_us["router_aux"] = timed(
             lambda: moe.router_aux(cfg, x, w_r, bias, idx2, gate2, 1e-2, aux_t, ws, stream), R)
+    # backward of the layer (training): gradients for an upstream dy, after the forward above
+    # (ws holds the forward results of the last timed step)
+    dy_t = torch.randn((wl.T, wl.d_model), device=dev).to(y.dtype)
+    dx_t = torch.empty_like(dy_t)
+    dw1_t, dw2_t = torch.empty_like(w1), torch.empty_like(w2)
+    dwr_t = torch.empty((wl.E, wl.d_model), dtype=torch.float32, device=dev) if wl.route == "topk" else None
+    dbias_t = torch.empty(wl.E, dtype=torch.float32, device=dev) if bias is not None else None
+    bws = moe.alloc_backward_workspace(cfg, dev)
+    kern_us["backward"] = timed(lambda: moe.backward(cfg, x, w_r, bias, w1, w2, dy_t, dx_t, dwr_t, dbias_t,
+                                                     dw1_t, dw2_t, ws, bws, stream), max(2, R // 2))
+    del dw1_t, dw2_t, bws
     try:  # the single-launch FFN, where its shape conditions hold
         kern_us["ffn_fused"] = timed(lambda: moe.expert_ffn_fused(cfg, x_e, cnt_t, w1, w2, y_e, stream), R)
     except moe.MoeError:

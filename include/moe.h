@@ -210,6 +210,36 @@ int moe_forward(const moe_config* cfg, const void* x, const float* w_r, const fl
                 const int32_t* group_id, const void* w1, const void* w2, void* y, void* ws,
                 void* stream);
 
+/* Bytes of the second device workspace moe_backward needs (`bws`: its scratch;
+ * the forward workspace `ws` keeps the forward's results).  Negative status on an
+ * invalid configuration. */
+int64_t moe_backward_workspace_bytes(const moe_config* cfg);
+
+/* Backward pass of the whole layer (training): gradients of a loss L through
+ * y = sum over served choices c of p_{i_c}(x) E_{i_c}(x) (Switch notes 2.1,
+ * Eq. 2; the gate keeps the router differentiable), E_i = act(x W1_i) W2_i and
+ * p = softmax(W_r x + bias) (Eq. 1).  The chosen experts and the capacity drop
+ * (2.2) are piecewise constant: no gradient flows through them and a dropped
+ * choice contributes nothing.  Random routed experts have constant gates 1, so
+ * the router gets no gradient (w_r, bias, dw_r, dbias are ignored).
+ * Precondition: `ws` holds the results of moe_forward on the same cfg, x, w_r,
+ * bias, w1 and w2 (routing, slots, x_e, hidden activations and y_e); the
+ * router is run again here and rewrites identical values into `ws`.
+ *   dy    [T, d_model] dtype: dL/dy
+ *   dx    [T, d_model] dtype out: dL/dx (expert path plus router path)
+ *   dw_r  [E, d_model] float32 out (learned routing): dL/dW_r
+ *   dbias [E] float32 out or NULL: dL/dbias (the sum of dL/dh over tokens)
+ *   dw1   [E, d_ff, d_model], dw2 [E, d_model, d_ff] dtype out: dL/dw1, dL/dw2
+ *         (every element written; zero for experts that served no token)
+ *   bws   workspace of moe_backward_workspace_bytes(cfg) bytes.
+ * bf16: products on bf16 MFMA with float32 accumulation; dy_e = gate * dy, dZ,
+ * dx_e and the outputs are rounded to bf16; the GELU pre-activation is
+ * recomputed in bf16.  The router gradient is float32; its token contraction is
+ * split into 16 ranges added in order, so repeated calls give identical bits. */
+int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
+                 const void* w1, const void* w2, const void* dy, void* dx, float* dw_r,
+                 float* dbias, void* dw1, void* dw2, void* ws, void* bws, void* stream);
+
 /* Message of the last non-OK status on this thread ("" if none). */
 const char* moe_last_error(void);
 

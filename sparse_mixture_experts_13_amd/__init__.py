@@ -19,7 +19,8 @@ from ._lib import ACT, DTYPE, EXPORTS, REGION, ROUTE, MoeConfig, load  # noqa: F
 
 __all__ = ["MoeConfig", "MoeError", "make_config", "config_for", "capacity", "workspace_bytes",
            "workspace_offset", "alloc_workspace", "workspace_view", "router", "router_aux", "dispatch",
-           "expert_ffn", "expert_ffn_fused", "expert_up", "expert_down", "combine", "forward", "version", "load"]
+           "expert_ffn", "expert_ffn_fused", "expert_up", "expert_down", "combine", "forward", "backward_workspace_bytes", "alloc_backward_workspace",
+           "backward", "version", "load"]
 
 
 class MoeError(RuntimeError):
@@ -148,6 +149,25 @@ def expert_down(cfg, hidden, expert_count, w2, y_e, stream=None) -> None:
 def combine(cfg, y_e, expert_idx, slot, gate, y, stream=None) -> None:
     _status(load().moe_combine(ctypes.byref(cfg), _ptr(y_e), _ptr(expert_idx), _ptr(slot),
                                _ptr(gate), _ptr(y), _stream(stream)))
+
+
+def backward_workspace_bytes(cfg: MoeConfig) -> int:
+    n = load().moe_backward_workspace_bytes(ctypes.byref(cfg))
+    if n < 0:
+        _status(int(n))
+    return int(n)
+
+
+def alloc_backward_workspace(cfg, device="cuda"):
+    """A uint8 device tensor of moe_backward_workspace_bytes(cfg) bytes."""
+    import torch
+    return torch.empty(max(backward_workspace_bytes(cfg), 1), dtype=torch.uint8, device=device)
+
+
+def backward(cfg, x, w_r, bias, w1, w2, dy, dx, dw_r, dbias, dw1, dw2, ws, bws, stream=None) -> None:
+    _status(load().moe_backward(ctypes.byref(cfg), _ptr(x), _ptr(w_r), _ptr(bias), _ptr(w1), _ptr(w2),
+                                _ptr(dy), _ptr(dx), _ptr(dw_r), _ptr(dbias), _ptr(dw1), _ptr(dw2),
+                                _ptr(ws), _ptr(bws), _stream(stream)))
 
 
 def forward(cfg, x, w_r, bias, group_id, w1, w2, y, ws, stream=None) -> None:

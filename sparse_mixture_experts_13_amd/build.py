@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["router.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["router.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip", "backward.hip", "moe_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,654 @@
+// Backward pass of the layer: gradients of y = sum over served choices of
+// p_i(x) E_i(x) (Switch Transformers notes, section 2.1, Eq. 2; the gate keeps
+// the router differentiable), with E_i(x) = act(x W1_i) W2_i and p = softmax(h)
+// of the router logits h = W_r x (+ bias) (Eq. 1).  The chosen set and the
+// capacity drop (section 2.2) are piecewise constant: no gradient flows
+// through them, and a dropped choice contributes nothing.
+//
+// Given dy = dL/dy, per served choice (token t, expert e, slot s):
+//   dy_e[e,s] = p * dy[t]                    dgate[t,c] = dy[t] . y_e[e,s]
+//   dZ = (dy_e W2_e^T-contraction) * act'(Z)  i.e. dZ[s,f] = sum_d dy_e[s,d] w2[e][d][f] * act'(Z[s,f])
+//   dx_e[s,d] = sum_f dZ[s,f] w1[e][f][d]
+//   dw2[e][d][f] = sum_s dy_e[s,d] H[s,f]    dw1[e][f][d] = sum_s dZ[s,f] x_e[s,d]
+//   router: dp_e = sum of dgate over the choices of e, dh = p (dp - <p, dp>),
+//           dx += dh W_r, dw_r = dh^T x, dbias = sum_t dh
+//   dx[t] = sum over served choices of dx_e[e,s], plus the router term.
+//
+// gfx950 design.  Scatter, softmax-Jacobian and final gather are one wave per
+// token.  All four expert products run on one grouped GEMM kernel with operand
+// orientation as template flags: an operand stored k-contiguous is staged in
+// LDS as [row][k] and read as 16-byte MFMA fragments; an operand stored
+// row-contiguous (the weights in dH = dy_e . w2 and dx_e = dZ . w1, and both
+// token-major operands of the weight gradients, whose contraction runs over
+// the tokens of an expert) is staged as [k][row] with 16-byte stores and read
+// as eight 2-byte values per fragment.  Register-staged double buffering,
+// 32-k steps, v_mfma_f32_32x32x16_bf16 with float32 accumulation, D = B . A^T
+// so each lane stores four consecutive output columns.  act' is applied in the
+// dH epilogue (from the hidden activation for ReLU, from the recomputed
+// pre-activation for GELU).  The router products (K = E or K = T) and the
+// float32 layers use a float32 FMA tile kernel with the same orientation
+// flags; the token-contracted router weight gradient is split over 16 token
+// ranges and the ranges are added in order (deterministic, no atomics).
+#include "moe_common.h"
+#include "moe_internal.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// dy_e = gate * dy (expert-major) and dgate = dy . y_e; one wave per token
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_scatter_kernel(
+    const T* __restrict__ dy, const T* __restrict__ y_e, const int32_t* __restrict__ expert_idx,
+    const int32_t* __restrict__ slot, const float* __restrict__ gate, int ntok, int E, int k,
+    int64_t C, int64_t d, T* __restrict__ dy_e, float* __restrict__ dgate) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const T* drow = dy + static_cast<int64_t>(t) * d;
+  for (int c = 0; c < k; ++c) {
+    const int64_t o = static_cast<int64_t>(t) * k + c;
+    const int s = slot[o];
+    const int e = expert_idx[o];
+    if (!(s >= 0 && s < C && e >= 0 && e < E)) {
+      if (lane == 0) dgate[o] = 0.f;
+      continue;
+    }
+    const float g = gate[o];
+    const int64_t row = (static_cast<int64_t>(e) * C + s) * d;
+    float dot = 0.f;
+    for (int64_t v = lane; v < d / 8; v += kWave) {
+      float a[8], b[8];
+      vec8<T>::load(drow + v * 8, a);
+      vec8<T>::load(y_e + row + v * 8, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot = fmaf(a[i], b[i], dot);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = g * a[i];
+      vec8<T>::store(dy_e + row + v * 8, a);
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) dgate[o] = dot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Softmax Jacobian: logits row -> dh = p * (dp - <p, dp>), in place (float32,
+// p computed as in the forward router: exp(h - max) / sum); one wave per token
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_router_softmax_kernel(
+    float* __restrict__ hrow, int ldh, const int32_t* __restrict__ expert_idx,
+    const int32_t* __restrict__ slot, const float* __restrict__ dgate, int ntok, int E, int k) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  float* row = hrow + static_cast<int64_t>(t) * ldh;
+  constexpr int NV = kMaxE / kWave;
+  float h[NV], dp[NV];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + kWave * i;
+    h[i] = e < E ? row[e] : -INFINITY;
+    dp[i] = 0.f;
+    m = fmaxf(m, h[i]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  for (int c = 0; c < k; ++c) {
+    const int64_t o = static_cast<int64_t>(t) * k + c;
+    const int e = expert_idx[o];
+    if (slot[o] >= 0 && e >= 0 && e < E) {
+      const float g = dgate[o];
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (lane + kWave * i == e) dp[i] += g;
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sum += expf(h[i] - m);  // exp(-inf) = 0
+  sum = wave_sum(sum);
+  float p[NV], pd = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    p[i] = expf(h[i] - m) / sum;
+    pd = fmaf(p[i], dp[i], pd);
+  }
+  pd = wave_sum(pd);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + kWave * i;
+    if (e < ldh) row[e] = e < E ? p[i] * (dp[i] - pd) : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dx[t] = sum over served choices of dx_e[e, s] (+ the router term, float32)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_gather_kernel(
+    const T* __restrict__ dx_e, const float* __restrict__ dx_r, const int32_t* __restrict__ expert_idx,
+    const int32_t* __restrict__ slot, int ntok, int E, int k, int64_t C, int64_t d,
+    T* __restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  int64_t off[kMaxK];
+#pragma unroll
+  for (int c = 0; c < kMaxK; ++c) {
+    off[c] = -1;
+    if (c < k) {
+      const int64_t o = static_cast<int64_t>(t) * k + c;
+      const int s = slot[o], e = expert_idx[o];
+      if (s >= 0 && s < C && e >= 0 && e < E) off[c] = (static_cast<int64_t>(e) * C + s) * d;
+    }
+  }
+  for (int64_t v = lane; v < d / 8; v += kWave) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxK; ++c) {
+      if (off[c] >= 0) {
+        float r[8];
+        vec8<T>::load(dx_e + off[c] + v * 8, r);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += r[i];
+      }
+    }
+    if (dx_r) {
+      float r[8];
+      vec8<float>::load(dx_r + static_cast<int64_t>(t) * d + v * 8, r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += r[i];
+    }
+    vec8<T>::store(dx + static_cast<int64_t>(t) * d + v * 8, acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM with operand orientation flags (bf16, MFMA).
+//   out[e][m][n] = epi( sum_k A(e, m, k) B(e, n, k) )
+//   A(e,m,k) = A[e * sAe + (AKC ? m * lda + k : k * lda + m)], same for B.
+// Per expert e: rows m < M_e, columns n < N, k < K_e, where either M_e or K_e
+// is the expert's token count (clamped to C) and the other is fixed; with
+// M_e = count, M is the row extent of the buffers (C), read but not stored past
+// the count.  Loads past the valid k range read as zero.  A K_e = 0 expert
+// stores zeros (weight gradients of an expert with no tokens).
+// EPI 0: store bf16(acc).  EPI 1: bf16(acc * act'(z)) with z read from `aux`
+// at the output position (ACT 0: z is the hidden activation, act' = z > 0;
+// ACT 1: z is the pre-activation, act' = GELU derivative).
+// ---------------------------------------------------------------------------
+constexpr int GBK2 = 32;
+
+__device__ __forceinline__ float gelu_grad(float z) {
+  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
+  const float pdf = expf(-0.5f * z * z) * 0.39894228040143268f;
+  return fmaf(z, pdf, cdf);
+}
+
+template <int ROWS, bool KC>
+struct OpTile {
+  // LDS elements per buffer: [ROWS][GBK2 + 8] (k-contiguous) or [GBK2][ROWS + 8]
+  static constexpr int kPitch = KC ? GBK2 + 8 : ROWS + 8;
+  static constexpr int kElems = KC ? ROWS * (GBK2 + 8) : GBK2 * (ROWS + 8);
+  static constexpr int kChunks = ROWS * GBK2 / 8;  // 16-byte chunks per tile
+};
+
+template <int BM, int BN, bool AKC, bool BKC, int EPI, int ACT>
+__global__ __launch_bounds__(256) void bgemm_kernel(
+    const bf16_t* __restrict__ A, int64_t sAe, int lda, const bf16_t* __restrict__ B, int64_t sBe,
+    int ldb, bf16_t* __restrict__ out, int64_t sOe, int ldo, const bf16_t* __restrict__ aux,
+    const int32_t* __restrict__ count, int64_t C, int M, int N, int K, bool m_is_count) {
+  using TA = OpTile<BM, AKC>;
+  using TBt = OpTile<BN, BKC>;
+  static_assert(TA::kChunks % 256 == 0 && TBt::kChunks % 256 == 0, "chunk split");
+  constexpr int CA = TA::kChunks / 256, CB = TBt::kChunks / 256;
+  constexpr int TM = BM / 64, TN = BN / 64;  // 32-row MFMA tiles per wave (2 x 2 waves)
+  __shared__ __align__(16) bf16_t la[2][TA::kElems];
+  __shared__ __align__(16) bf16_t lb[2][TBt::kElems];
+
+  const int e = blockIdx.z;
+  int64_t cnt = count[e];
+  cnt = cnt < 0 ? 0 : (cnt > C ? C : cnt);
+  const int Mv = m_is_count ? static_cast<int>(cnt) : M;
+  const int Kv = m_is_count ? K : static_cast<int>(cnt);
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  if (m0 >= Mv) return;
+  const bf16_t* Ae = A + e * sAe;
+  const bf16_t* Be = B + e * sBe;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, fr = lane & 31;
+
+  u32x4 ra[CA], rb[CB];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int q = tid + 256 * i;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if constexpr (AKC) {
+        const int r = q / (GBK2 / 8), kc = q % (GBK2 / 8);
+        const int m = m0 + r, kk = k0 + kc * 8;
+        if (m < M && kk < Kv) v = *reinterpret_cast<const u32x4*>(Ae + static_cast<int64_t>(m) * lda + kk);
+      } else {
+        const int kr = q / (BM / 8), mc = q % (BM / 8);
+        const int kk = k0 + kr, m = m0 + mc * 8;
+        if (kk < Kv && m < M) v = *reinterpret_cast<const u32x4*>(Ae + static_cast<int64_t>(kk) * lda + m);
+      }
+      ra[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int q = tid + 256 * i;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if constexpr (BKC) {
+        const int r = q / (GBK2 / 8), kc = q % (GBK2 / 8);
+        const int n = n0 + r, kk = k0 + kc * 8;
+        if (n < N && kk < Kv) v = *reinterpret_cast<const u32x4*>(Be + static_cast<int64_t>(n) * ldb + kk);
+      } else {
+        const int kr = q / (BN / 8), nc = q % (BN / 8);
+        const int kk = k0 + kr, n = n0 + nc * 8;
+        if (kk < Kv && n < N) v = *reinterpret_cast<const u32x4*>(Be + static_cast<int64_t>(kk) * ldb + n);
+      }
+      rb[i] = v;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      const int q = tid + 256 * i;
+      const int idx = AKC ? (q / (GBK2 / 8)) * TA::kPitch + (q % (GBK2 / 8)) * 8
+                          : (q / (BM / 8)) * TA::kPitch + (q % (BM / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&la[buf][idx]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int q = tid + 256 * i;
+      const int idx = BKC ? (q / (GBK2 / 8)) * TBt::kPitch + (q % (GBK2 / 8)) * 8
+                          : (q / (BN / 8)) * TBt::kPitch + (q % (BN / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&lb[buf][idx]) = rb[i];
+    }
+  };
+  // fragment of operand rows r (32 rows starting at r0), k = 16 j + 8 half .. + 7
+  auto frag = [&](const bf16_t* t, bool kc, int pitch, int r, int j) {
+    const int k = 16 * j + 8 * half;
+    if (kc) return *reinterpret_cast<const bf16x8*>(t + r * pitch + k);
+    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+    u16x8 v;  // raw bits: a bf16 vector element would convert the integer's value
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = t[(k + i) * pitch + r];
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  floatx16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
+
+  const int nk = (Kv + GBK2 - 1) / GBK2;
+  if (nk > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) load((kt + 1) * GBK2);
+#pragma unroll
+      for (int j = 0; j < GBK2 / 16; ++j) {
+        bf16x8 fa[TM], fb[TN];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) fa[t] = frag(la[buf], AKC, TA::kPitch, (wm * TM + t) * 32 + fr, j);
+#pragma unroll
+        for (int i = 0; i < TN; ++i) fb[i] = frag(lb[buf], BKC, TBt::kPitch, (wn * TN + i) * 32 + fr, j);
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int t = 0; t < TM; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i], fa[t], acc[i][t], 0, 0, 0);
+      }
+      if (kt + 1 < nk) store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  // D[n][m]: lane holds m = fr and n = 8 * (r / 4) + 4 * half + r % 4 of each 32 x 32 tile
+  bf16_t* Oe = out + e * sOe;
+  const bf16_t* Ze = aux ? aux + e * sOe : nullptr;
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    const int m = m0 + (wm * TM + t) * 32 + fr;
+    if (m >= Mv) continue;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int nt0 = n0 + (wn * TN + i) * 32;
+      if (nt0 >= N) continue;  // N % 32 == 0
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nt0 + 8 * q + 4 * half;
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = acc[i][t][4 * q + u];
+        if constexpr (EPI == 1) {
+          const uint2 zz = *reinterpret_cast<const uint2*>(Ze + static_cast<int64_t>(m) * ldo + n);
+          const float z[4] = {__uint_as_float(zz.x << 16), __uint_as_float(zz.x & 0xFFFF0000u),
+                              __uint_as_float(zz.y << 16), __uint_as_float(zz.y & 0xFFFF0000u)};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] *= ACT == 0 ? (z[u] > 0.f ? 1.f : 0.f) : gelu_grad(z[u]);
+        }
+        uint2 w;
+        w.x = pack_bf16x2(v[0], v[1]);
+        w.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(Oe + static_cast<int64_t>(m) * ldo + n) = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 FMA tile GEMM with the same orientation flags, 64 x 64 tile, BK 16,
+// 4 x 4 outputs per thread.  Inputs of type TA / TB (float or bf16), float32
+// accumulation, output float32 or TO.  Batched over z = e * KS + ks: KS > 1
+// splits the k range into KS contiguous pieces, piece ks going to output slice
+// ks (out + ks * sOk), added later in order.  Per expert e: M_e / K_e as in
+// bgemm_kernel (count == nullptr: every expert has the fixed M and K).
+// ---------------------------------------------------------------------------
+template <typename T> __device__ __forceinline__ float ld_f32(const T* p);
+template <> __device__ __forceinline__ float ld_f32<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld_f32<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+template <typename T> __device__ __forceinline__ void st_f32(T* p, float v);
+template <> __device__ __forceinline__ void st_f32<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st_f32<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+template <typename TA, typename TB, typename TO, bool AKC, bool BKC, int EPI, int ACT>
+__global__ __launch_bounds__(256) void fgemm_kernel(
+    const TA* __restrict__ A, int64_t sAe, int lda, const TB* __restrict__ B, int64_t sBe, int ldb,
+    TO* __restrict__ out, int64_t sOe, int64_t sOk, int ldo, const TO* __restrict__ aux,
+    const int32_t* __restrict__ count, int64_t C, int M, int N, int K, bool m_is_count, int KS) {
+  __shared__ float sa[16][65];
+  __shared__ float sb[16][65];
+  const int e = blockIdx.z / KS, ks = blockIdx.z % KS;
+  int Mv = M, Kv = K;
+  if (count) {
+    int64_t cnt = count[e];
+    cnt = cnt < 0 ? 0 : (cnt > C ? C : cnt);
+    if (m_is_count) Mv = static_cast<int>(cnt);
+    else Kv = static_cast<int>(cnt);
+  }
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  if (m0 >= Mv) return;
+  const int kb = static_cast<int>(static_cast<int64_t>(ks) * Kv / KS);
+  const int ke = static_cast<int>(static_cast<int64_t>(ks + 1) * Kv / KS);
+  const TA* Ae = A + e * sAe;
+  const TB* Be = B + e * sBe;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = kb; k0 < ke; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;
+      // tile element (row r in 0..63, k c in 0..15); which index runs fastest
+      // follows the storage so that neighbouring threads read neighbouring memory
+      const int r = AKC ? q >> 4 : q & 63, c = AKC ? q & 15 : q >> 6;
+      const int m = m0 + r, kk = k0 + c;
+      sa[c][r] = (m < M && kk < ke) ? ld_f32(Ae + (AKC ? static_cast<int64_t>(m) * lda + kk
+                                                       : static_cast<int64_t>(kk) * lda + m)) : 0.f;
+      const int r2 = BKC ? q >> 4 : q & 63, c2 = BKC ? q & 15 : q >> 6;
+      const int n = n0 + r2, kk2 = k0 + c2;
+      sb[c2][r2] = (n < N && kk2 < ke) ? ld_f32(Be + (BKC ? static_cast<int64_t>(n) * ldb + kk2
+                                                          : static_cast<int64_t>(kk2) * ldb + n)) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sa[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sb[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  TO* Oe = out + e * sOe + ks * sOk;
+  const TO* Ze = aux ? aux + e * sOe : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty + 16 * i;
+    if (m >= Mv) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx + 16 * j;
+      if (n >= N) continue;
+      float v = acc[i][j];
+      if constexpr (EPI == 1) {
+        const float z = ld_f32(Ze + static_cast<int64_t>(m) * ldo + n);
+        v *= ACT == 0 ? (z > 0.f ? 1.f : 0.f) : gelu_grad(z);
+      }
+      st_f32(Oe + static_cast<int64_t>(m) * ldo + n, v);
+    }
+  }
+}
+
+// Add KS float slices in order: out[i] = ((s0 + s1) + s2) + ...
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ part, int64_t n,
+                                                         int KS, float* __restrict__ out) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float v = part[i];
+    for (int s = 1; s < KS; ++s) v += part[s * n + i];
+    out[i] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0.f;
+}
+
+// dbias[e] = sum over tokens of dh[t][e] in token order, 16 tokens in flight
+__global__ __launch_bounds__(64) void bwd_bias_kernel(const float* __restrict__ dh, int ldh, int ntok,
+                                                      int E, float* __restrict__ dbias) {
+  const int e = blockIdx.x * 64 + threadIdx.x;
+  if (e >= E) return;
+  float acc = 0.f;
+  for (int t = 0; t < ntok; t += 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = t + j < ntok ? dh[static_cast<int64_t>(t + j) * ldh + e] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc += v[j];
+  }
+  dbias[e] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <int BM, int BN, bool AKC, bool BKC, int EPI, int ACT>
+static hipError_t run_bgemm(const Plan& p, const bf16_t* A, int64_t sAe, int lda, const bf16_t* B,
+                            int64_t sBe, int ldb, bf16_t* out, int64_t sOe, int ldo,
+                            const bf16_t* aux, const int32_t* count, int M, int N, int K,
+                            bool m_is_count, hipStream_t s) {
+  const int mtiles = ((m_is_count ? static_cast<int>(p.C) : M) + BM - 1) / BM;
+  const dim3 grid((N + BN - 1) / BN, mtiles, p.E);
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  hipLaunchKernelGGL((bgemm_kernel<BM, BN, AKC, BKC, EPI, ACT>), grid, dim3(256), 0, s, A, sAe, lda, B,
+                     sBe, ldb, out, sOe, ldo, aux, count, p.C, M, N, K, m_is_count);
+  return hipGetLastError();
+}
+
+template <typename TA, typename TB, typename TO, bool AKC, bool BKC, int EPI, int ACT>
+static hipError_t run_fgemm(int batch, int64_t C, const TA* A, int64_t sAe, int lda, const TB* B,
+                            int64_t sBe, int ldb, TO* out, int64_t sOe, int64_t sOk, int ldo,
+                            const TO* aux, const int32_t* count, int M, int N, int K,
+                            bool m_is_count, int KS, hipStream_t s) {
+  const int mtiles = ((m_is_count && count ? static_cast<int>(C) : M) + 63) / 64;
+  const dim3 grid((N + 63) / 64, mtiles, batch * KS);
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+  hipLaunchKernelGGL((fgemm_kernel<TA, TB, TO, AKC, BKC, EPI, ACT>), grid, dim3(256), 0, s, A, sAe,
+                     lda, B, sBe, ldb, out, sOe, sOk, ldo, aux, count, C, M, N, K, m_is_count, KS);
+  return hipGetLastError();
+}
+
+#define MOE_TRY(x)                         \
+  do {                                     \
+    const hipError_t err_ = (x);           \
+    if (err_ != hipSuccess) return err_;   \
+  } while (0)
+
+// Expert-side products for one dtype.  dZ is staged in the dZ buffer, the
+// pre-activation (GELU) in the Z buffer.
+template <typename T>
+static hipError_t expert_backward(const Plan& p, const T* x_e, const T* hidden, const T* w1,
+                                  const T* w2, const int32_t* count, const T* dy_e, T* zbuf,
+                                  T* dz, T* dx_e, T* dw1, T* dw2, hipStream_t s);
+
+template <>
+hipError_t expert_backward<bf16_t>(const Plan& p, const bf16_t* x_e, const bf16_t* hidden,
+                                   const bf16_t* w1, const bf16_t* w2, const int32_t* count,
+                                   const bf16_t* dy_e, bf16_t* zbuf, bf16_t* dz, bf16_t* dx_e,
+                                   bf16_t* dw1, bf16_t* dw2, hipStream_t s) {
+  const int d = static_cast<int>(p.d), f = static_cast<int>(p.f);
+  const int64_t C = p.C, sX = C * d, sH = C * f, sW = int64_t(d) * f;
+  const int Ci = static_cast<int>(C);
+  // GELU: pre-activation Z = x_e . w1^T again (the forward keeps only act(Z))
+  if (p.act == 1) MOE_TRY(launch_expert_up_act(p, x_e, count, w1, zbuf, 2, s));
+  const bf16_t* z = p.act == 1 ? zbuf : hidden;
+  // dZ[s][f] = sum_d dy_e[s][d] w2[d][f] * act'(Z)   (A = dy_e k-contiguous, B = w2 [k=d][n=f])
+  if (p.act == 0)
+    MOE_TRY((run_bgemm<64, 128, true, false, 1, 0>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
+                                                    f, d, true, s)));
+  else
+    MOE_TRY((run_bgemm<64, 128, true, false, 1, 1>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
+                                                    f, d, true, s)));
+  // dx_e[s][d] = sum_f dZ[s][f] w1[f][d]   (B = w1 [k=f][n=d])
+  MOE_TRY((run_bgemm<64, 128, true, false, 0, 0>(p, dz, sH, f, w1, sW, d, dx_e, sX, d, nullptr, count,
+                                                  Ci, d, f, true, s)));
+  // dw2[d][f] = sum_s dy_e[s][d] H[s][f]   (A = dy_e [k=s][m=d], B = H [k=s][n=f])
+  MOE_TRY((run_bgemm<128, 128, false, false, 0, 0>(p, dy_e, sX, d, hidden, sH, f, dw2, sW, f, nullptr,
+                                                    count, d, f, 0, false, s)));
+  // dw1[f][d] = sum_s dZ[s][f] x_e[s][d]
+  MOE_TRY((run_bgemm<128, 128, false, false, 0, 0>(p, dz, sH, f, x_e, sX, d, dw1, sW, d, nullptr, count,
+                                                    f, d, 0, false, s)));
+  return hipSuccess;
+}
+
+template <>
+hipError_t expert_backward<float>(const Plan& p, const float* x_e, const float* hidden,
+                                  const float* w1, const float* w2, const int32_t* count,
+                                  const float* dy_e, float* zbuf, float* dz, float* dx_e, float* dw1,
+                                  float* dw2, hipStream_t s) {
+  const int d = static_cast<int>(p.d), f = static_cast<int>(p.f);
+  const int64_t C = p.C, sX = C * d, sH = C * f, sW = int64_t(d) * f;
+  const int Ci = static_cast<int>(C);
+  if (p.act == 1) MOE_TRY(launch_expert_up_act(p, x_e, count, w1, zbuf, 2, s));
+  const float* z = p.act == 1 ? zbuf : hidden;
+  if (p.act == 0)
+    MOE_TRY((run_fgemm<float, float, float, true, false, 1, 0>(p.E, C, dy_e, sX, d, w2, sW, f, dz, sH, 0,
+                                                                f, z, count, Ci, f, d, true, 1, s)));
+  else
+    MOE_TRY((run_fgemm<float, float, float, true, false, 1, 1>(p.E, C, dy_e, sX, d, w2, sW, f, dz, sH, 0,
+                                                                f, z, count, Ci, f, d, true, 1, s)));
+  MOE_TRY((run_fgemm<float, float, float, true, false, 0, 0>(p.E, C, dz, sH, f, w1, sW, d, dx_e, sX, 0, d,
+                                                              nullptr, count, Ci, d, f, true, 1, s)));
+  MOE_TRY((run_fgemm<float, float, float, false, false, 0, 0>(p.E, C, dy_e, sX, d, hidden, sH, f, dw2, sW,
+                                                               0, f, nullptr, count, d, f, 0, false, 1, s)));
+  MOE_TRY((run_fgemm<float, float, float, false, false, 0, 0>(p.E, C, dz, sH, f, x_e, sX, d, dw1, sW, 0,
+                                                               d, nullptr, count, f, d, 0, false, 1, s)));
+  return hipSuccess;
+}
+
+template <typename T>
+static hipError_t backward_typed(const Plan& p, const BwdArgs& a, hipStream_t s) {
+  const int d = static_cast<int>(p.d);
+  const int T_ = static_cast<int>(p.T);
+  const int nblk = static_cast<int>((p.T + 3) / 4);
+  const T* dy = static_cast<const T*>(a.dy);
+  T* dy_e = static_cast<T*>(a.dy_e);
+  if (p.T > 0)
+    hipLaunchKernelGGL(bwd_scatter_kernel<T>, dim3(nblk), dim3(256), 0, s, dy,
+                       static_cast<const T*>(a.y_e), a.expert_idx, a.slot, a.gate, T_, p.E, p.k,
+                       p.C, p.d, dy_e, a.dgate);
+  MOE_TRY(hipGetLastError());
+  if (p.C > 0)
+    MOE_TRY(expert_backward<T>(p, static_cast<const T*>(a.x_e), static_cast<const T*>(a.hidden),
+                               static_cast<const T*>(a.w1), static_cast<const T*>(a.w2), a.count, dy_e,
+                               static_cast<T*>(a.zbuf), static_cast<T*>(a.dz), static_cast<T*>(a.dx_e),
+                               static_cast<T*>(a.dw1), static_cast<T*>(a.dw2), s));
+  else {
+    // no capacity: every weight gradient is zero (sizes are multiples of 64 elements)
+    const int64_t n16 = int64_t(p.E) * p.d * p.f * p.elem / 16;
+    const unsigned g = static_cast<unsigned>(std::min<int64_t>((n16 + 255) / 256, 4096));
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(g), dim3(256), 0, s, static_cast<u32x4*>(a.dw1), n16);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(g), dim3(256), 0, s, static_cast<u32x4*>(a.dw2), n16);
+    MOE_TRY(hipGetLastError());
+  }
+  float* dx_r = nullptr;
+  if (p.route == 0 && p.T > 0) {
+    // router: logits again (same kernel and arithmetic as the forward), softmax Jacobian
+    MOE_TRY(launch_router_topk(p, a.x, a.w_r, a.bias, a.idx_scratch, a.gate_scratch, a.ws, s, false,
+                               a.dh));
+    hipLaunchKernelGGL(bwd_router_softmax_kernel, dim3(nblk), dim3(256), 0, s, a.dh, p.Epad,
+                       a.expert_idx, a.slot, a.dgate, T_, p.E, p.k);
+    MOE_TRY(hipGetLastError());
+    // dx_r[t][d] = sum_e dh[t][e] w_r[e][d]
+    dx_r = a.dx_r;
+    MOE_TRY((run_fgemm<float, float, float, true, false, 0, 0>(1, 0, a.dh, 0, p.Epad, a.w_r, 0, d, dx_r, 0,
+                                                                0, d, nullptr, nullptr, T_, d, p.E, false, 1,
+                                                                s)));
+    // dw_r[e][d] = sum_t dh[t][e] x[t][d], in kBwdSplit token ranges added in order
+    const int64_t n = int64_t(p.E) * d;
+    MOE_TRY((run_fgemm<float, T, float, false, false, 0, 0>(1, 0, a.dh, 0, p.Epad, static_cast<const T*>(a.x),
+                                                             0, d, a.dwr_part, 0, n, d, nullptr, nullptr,
+                                                             p.E, d, T_, false, kBwdSplit, s)));
+    hipLaunchKernelGGL(sum_slices_kernel, dim3(static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 1024))),
+                       dim3(256), 0, s, a.dwr_part, n, kBwdSplit, a.dw_r);
+    MOE_TRY(hipGetLastError());
+    if (a.dbias) {
+      hipLaunchKernelGGL(bwd_bias_kernel, dim3((p.E + 63) / 64), dim3(64), 0, s, a.dh, p.Epad, T_, p.E,
+                         a.dbias);
+      MOE_TRY(hipGetLastError());
+    }
+  }
+  if (p.route == 0 && p.T == 0) {
+    // no tokens: the router gradients are zero
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(64), dim3(256), 0, s, a.dw_r, int64_t(p.E) * d);
+    if (a.dbias) hipLaunchKernelGGL(zero_f32_kernel, dim3(1), dim3(256), 0, s, a.dbias, int64_t(p.E));
+    MOE_TRY(hipGetLastError());
+  }
+  if (p.T > 0)
+    hipLaunchKernelGGL(bwd_gather_kernel<T>, dim3(nblk), dim3(256), 0, s,
+                       static_cast<const T*>(a.dx_e), dx_r, a.expert_idx, a.slot, T_, p.E, p.k, p.C,
+                       p.d, static_cast<T*>(a.dx));
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t s) {
+  return p.dtype == 1 ? backward_typed<bf16_t>(p, a, s) : backward_typed<float>(p, a, s);
+}
+
+#undef MOE_TRY
+
+}  // namespace moe

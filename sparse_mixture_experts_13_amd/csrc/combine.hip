@@ -12,42 +12,6 @@
 namespace moe {
 
 template <typename T>
-struct vec8;  // eight elements as one or two 16-byte vectors
-template <>
-struct vec8<bf16_t> {
-  static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
-    const u32x4 r = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(r[i] << 16);
-      v[2 * i + 1] = __uint_as_float(r[i] & 0xFFFF0000u);
-    }
-  }
-  static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-    *reinterpret_cast<u32x4*>(p) = r;
-  }
-};
-template <>
-struct vec8<float> {
-  static __device__ __forceinline__ void load(const float* p, float* v) {
-    const floatx4 a = *reinterpret_cast<const floatx4*>(p);
-    const floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = a[i];
-      v[4 + i] = b[i];
-    }
-  }
-  static __device__ __forceinline__ void store(float* p, const float* v) {
-    *reinterpret_cast<floatx4*>(p) = floatx4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<floatx4*>(p + 4) = floatx4{v[4], v[5], v[6], v[7]};
-  }
-};
-
-template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_e,
                                                       const int32_t* __restrict__ expert_idx,
                                                       const int32_t* __restrict__ slot,

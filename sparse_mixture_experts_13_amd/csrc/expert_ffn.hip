@@ -821,6 +821,22 @@ hipError_t launch_expert_up(const Plan& p, const void* x_e, const int32_t* exper
                     : run_f32<1>(p.E, xe, w, h, expert_count, p.C, f, d, s);
 }
 
+hipError_t launch_expert_up_act(const Plan& p, const void* x_e, const int32_t* expert_count,
+                                const void* w1, void* out, int act, hipStream_t s) {
+  Plan q = p;
+  q.act = act;
+  if (act == 2) {  // no activation
+    if (p.C == 0) return hipSuccess;
+    const int d = static_cast<int>(p.d), f = static_cast<int>(p.f);
+    if (p.dtype == 1)
+      return gemm_bf16<2>(q, static_cast<const bf16_t*>(x_e), static_cast<const bf16_t*>(w1),
+                          static_cast<bf16_t*>(out), expert_count, f, d, s);
+    return run_f32<2>(p.E, static_cast<const float*>(x_e), static_cast<const float*>(w1),
+                      static_cast<float*>(out), expert_count, p.C, f, d, s);
+  }
+  return launch_expert_up(q, x_e, expert_count, w1, out, s);
+}
+
 hipError_t launch_expert_down(const Plan& p, const void* hidden, const int32_t* expert_count,
                               const void* w2, void* y_e, hipStream_t s) {
   if (p.C == 0) return hipSuccess;

@@ -128,6 +128,33 @@ void make_plan(const moe_config* cfg, moe::Plan& p) {
   p.total = off;
 }
 
+// Backward scratch (second workspace): byte offsets of its buffers.
+struct BwdLayout {
+  int64_t idx, gate, dgate, dy_e, zbuf, dz, dx_e, dh, dx_r, dwr_part, total;
+};
+
+void bwd_layout(const moe::Plan& p, BwdLayout& L) {
+  const int64_t Tk = p.T * p.k, EC = int64_t(p.E) * p.C;
+  const bool topk = p.route == MOE_ROUTE_TOPK;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.idx = take(Tk * 4);
+  L.gate = take(Tk * 4);
+  L.dgate = take(Tk * 4);
+  L.dy_e = take(EC * p.d * p.elem);
+  L.zbuf = take(p.act == MOE_ACT_GELU ? EC * p.f * p.elem : 0);
+  L.dz = take(EC * p.f * p.elem);
+  L.dx_e = take(EC * p.d * p.elem);
+  L.dh = take(topk ? p.T * p.Epad * 4 : 0);
+  L.dx_r = take(topk ? p.T * p.d * 4 : 0);
+  L.dwr_part = take(topk ? int64_t(moe::kBwdSplit) * p.E * p.d * 4 : 0);
+  L.total = off;
+}
+
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 // A required device buffer: non-NULL when it holds bytes, 16-byte aligned.
@@ -373,6 +400,76 @@ int moe_forward(const moe_config* cfg, const void* x, const float* w_r, const fl
           "dispatch slots/gather");
   MOE_HIP(moe::launch_expert_ffn(p, x_e, count, w1, w2, y_e, ws, s), "expert ffn");
   MOE_HIP(moe::launch_combine(p, y_e, expert_idx, slot, gate, y, s), "combine");
+  return MOE_OK;
+}
+
+int64_t moe_backward_workspace_bytes(const moe_config* cfg) {
+  const int rc = validate(cfg);
+  if (rc != MOE_OK) return rc;
+  moe::Plan p;
+  make_plan(cfg, p);
+  BwdLayout L;
+  bwd_layout(p, L);
+  return L.total;
+}
+
+int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
+                 const void* w1, const void* w2, const void* dy, void* dx, float* dw_r,
+                 float* dbias, void* dw1, void* dw2, void* ws, void* bws, void* stream) {
+  MOE_CHECK(validate(cfg));
+  moe::Plan p;
+  make_plan(cfg, p);
+  BwdLayout L;
+  bwd_layout(p, L);
+  const int64_t wbytes = int64_t(p.E) * p.d * p.f * p.elem;
+  const int64_t tbytes = p.T * p.d * p.elem;
+  const bool topk = p.route == MOE_ROUTE_TOPK;
+  MOE_CHECK(need(x, tbytes, "x"));
+  if (topk) {
+    MOE_CHECK(need(w_r, 1, "w_r"));
+    MOE_CHECK(need(dw_r, int64_t(p.E) * p.d * 4, "dw_r"));
+  }
+  MOE_CHECK(need(w1, wbytes, "w1"));
+  MOE_CHECK(need(w2, wbytes, "w2"));
+  MOE_CHECK(need(dy, tbytes, "dy"));
+  MOE_CHECK(need(dx, tbytes, "dx"));
+  MOE_CHECK(need(dw1, wbytes, "dw1"));
+  MOE_CHECK(need(dw2, wbytes, "dw2"));
+  MOE_CHECK(need(ws, p.total, "ws"));
+  MOE_CHECK(need(bws, L.total, "bws"));
+  char* base = static_cast<char*>(ws);
+  char* bb = static_cast<char*>(bws);
+  moe::BwdArgs a{};
+  a.x = x;
+  a.w_r = w_r;
+  a.bias = bias;
+  a.w1 = w1;
+  a.w2 = w2;
+  a.dy = dy;
+  a.dx = dx;
+  a.dw_r = topk ? dw_r : nullptr;
+  a.dbias = topk ? dbias : nullptr;
+  a.dw1 = dw1;
+  a.dw2 = dw2;
+  a.expert_idx = reinterpret_cast<const int32_t*>(base + p.off_region[MOE_WS_EXPERT_IDX]);
+  a.gate = reinterpret_cast<const float*>(base + p.off_region[MOE_WS_GATE]);
+  a.slot = reinterpret_cast<const int32_t*>(base + p.off_region[MOE_WS_SLOT]);
+  a.count = reinterpret_cast<const int32_t*>(base + p.off_region[MOE_WS_EXPERT_COUNT]);
+  a.x_e = base + p.off_region[MOE_WS_X_E];
+  a.hidden = base + p.off_region[MOE_WS_HIDDEN];
+  a.y_e = base + p.off_region[MOE_WS_Y_E];
+  a.ws = ws;
+  a.idx_scratch = reinterpret_cast<int32_t*>(bb + L.idx);
+  a.gate_scratch = reinterpret_cast<float*>(bb + L.gate);
+  a.dgate = reinterpret_cast<float*>(bb + L.dgate);
+  a.dy_e = bb + L.dy_e;
+  a.zbuf = bb + L.zbuf;
+  a.dz = bb + L.dz;
+  a.dx_e = bb + L.dx_e;
+  a.dh = reinterpret_cast<float*>(bb + L.dh);
+  a.dx_r = reinterpret_cast<float*>(bb + L.dx_r);
+  a.dwr_part = reinterpret_cast<float*>(bb + L.dwr_part);
+  MOE_HIP(moe::launch_backward(p, a, static_cast<hipStream_t>(stream)), "backward");
   return MOE_OK;
 }
 

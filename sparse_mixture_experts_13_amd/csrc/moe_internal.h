@@ -27,9 +27,10 @@ struct Plan {
 // router.hip
 hipError_t launch_router_split(const Plan& p, const float* w_r, void* ws, hipStream_t s);
 // with_psum: also write the per-block expert probability sums (load-balancing loss)
+// logits (may be null): also write the float32 logits (bias included) [T][Epad]
 hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, const float* bias,
                               int32_t* expert_idx, float* gate, void* ws, hipStream_t s,
-                              bool with_psum = false);
+                              bool with_psum = false, float* logits = nullptr);
 // aux = [alpha * E * sum_i f_i P_i, f[E], P[E]] from the router's block rows
 hipError_t launch_router_aux(const Plan& p, double alpha, float* aux, void* ws, hipStream_t s);
 // Load-balancing workspace: per router block a float row of Epad probability
@@ -61,6 +62,48 @@ hipError_t launch_expert_ffn_fused(const Plan& p, int nspl, const void* x_e,
                                    void* y_e, hipStream_t s);
 hipError_t launch_expert_down(const Plan& p, const void* hidden, const int32_t* expert_count,
                               const void* w2, void* y_e, hipStream_t s);
+
+// Up-projection with an explicit activation (2: none, for the pre-activation).
+hipError_t launch_expert_up_act(const Plan& p, const void* x_e, const int32_t* expert_count,
+                                const void* w1, void* out, int act, hipStream_t s);
+
+// backward.hip
+constexpr int kBwdSplit = 16;  // token ranges of the router weight gradient
+struct BwdArgs {
+  // inputs and outputs of the call
+  const void* x;
+  const float* w_r;
+  const float* bias;
+  const void* w1;
+  const void* w2;
+  const void* dy;
+  void* dx;
+  float* dw_r;
+  float* dbias;
+  void* dw1;
+  void* dw2;
+  // the forward's results (forward workspace)
+  const int32_t* expert_idx;
+  const float* gate;
+  const int32_t* slot;
+  const int32_t* count;
+  const void* x_e;
+  const void* hidden;
+  const void* y_e;
+  void* ws;
+  // backward scratch
+  int32_t* idx_scratch;
+  float* gate_scratch;
+  float* dgate;
+  void* dy_e;
+  void* zbuf;
+  void* dz;
+  void* dx_e;
+  float* dh;
+  float* dx_r;
+  float* dwr_part;
+};
+hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const Plan& p, const void* y_e, const int32_t* expert_idx,

@@ -56,7 +56,8 @@ __device__ __forceinline__ int key_expert(uint64_t key) {
 __device__ void topk_epilogue(const float* lg, int ld, int tok0, int ntok, int E, int k,
                               const float* __restrict__ bias, int32_t* __restrict__ expert_idx,
                               float* __restrict__ gate, int* hl, int ldh, int wave, int lane,
-                              float* __restrict__ psum, float* red) {
+                              float* __restrict__ psum, float* red, float* __restrict__ hout,
+                              int ldo) {
   const int nper = (E + kWave - 1) / kWave;  // <= 8
   float pacc[kMaxE / kWave];
 #pragma unroll
@@ -75,6 +76,7 @@ __device__ void topk_epilogue(const float* lg, int ld, int tok0, int ntok, int E
         if (bias) h = h + bias[e];  // one float32 rounding after the full dot product
         hv[i] = h;
         kv[i] = make_key(h, e);
+        if (hout) hout[static_cast<int64_t>(tok0 + t) * ldo + e] = h;
       }
     }
     uint64_t best0 = 0, bestc = 0;
@@ -182,7 +184,8 @@ template <int NV>
 __device__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int ntok, int E, int k,
                                 const float* __restrict__ bias, int32_t* __restrict__ expert_idx,
                                 float* __restrict__ gate, int* hl, int ldh, int wave, int lane,
-                                float* __restrict__ psum, float* red) {
+                                float* __restrict__ psum, float* red, float* __restrict__ hout,
+                                int ldo) {
   const int grp = lane >> 4, sub = lane & 15;
   float pacc[NV];
 #pragma unroll
@@ -199,6 +202,7 @@ __device__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int n
         float h = lg[t * ld + e];
         if (bias) h = h + bias[e];  // one float32 rounding after the full dot product
         hv[i] = h;
+        if (hout) hout[static_cast<int64_t>(tok0 + t) * ldo + e] = h;
       }
     }
     uint32_t removed = 0;
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, const int* __restrict__ flags,
     const float* __restrict__ bias, int T, int d, int E, int Epad, int k,
     int32_t* __restrict__ expert_idx, float* __restrict__ gate, int* __restrict__ hist, int NB,
-    float* __restrict__ psum) {
+    float* __restrict__ psum, float* __restrict__ hout) {
   constexpr int TB = 32 * TT;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   }
   __syncthreads();
   topk_epilogue16<8 * EW>(lg, ld, TB, tok0, ntok, E, k, bias, expert_idx, gate, hl, Epad, wave,
-                          lane, psum ? psum + static_cast<int64_t>(b) * Epad : nullptr, lg);
+                          lane, psum ? psum + static_cast<int64_t>(b) * Epad : nullptr, lg, hout, Epad);
   __syncthreads();
   write_hist(hl, Epad, E, k, NB, b, hist, tid, 256);
 }
@@ -392,7 +396,7 @@ template <int NACC>
 __global__ __launch_bounds__(256) void router_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ w_r, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ expert_idx, float* __restrict__ gate,
-    int* __restrict__ hist, int NB, float* __restrict__ psum, int ldp) {
+    int* __restrict__ hist, int NB, float* __restrict__ psum, int ldp, float* __restrict__ hout) {
   constexpr int Ecap = 4 * NACC;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
   for (int j = 0; j < NACC; ++j) lg[t * ld + eg + 4 * j] = acc[j];
   __syncthreads();
   topk_epilogue(lg, ld, tok0, ntok, E, k, bias, expert_idx, gate, hl, Ecap, wave, lane,
-                psum ? psum + static_cast<int64_t>(b) * ldp : nullptr, lg);
+                psum ? psum + static_cast<int64_t>(b) * ldp : nullptr, lg, hout, ldp);
   __syncthreads();
   write_hist(hl, Ecap, E, k, NB, b, hist, tid, 256);
 }
@@ -575,7 +579,7 @@ static hipError_t set_lds(K kernel, int64_t bytes) {
 
 hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, const float* bias,
                               int32_t* expert_idx, float* gate, void* ws, hipStream_t s,
-                              bool with_psum) {
+                              bool with_psum, float* logits) {
   if (p.T == 0) return hipSuccess;
   int* hist = reinterpret_cast<int*>(ws_at(ws, p.off_hist));
   float* psum = with_psum ? reinterpret_cast<float*>(ws_at(ws, p.off_psum)) : nullptr;
@@ -593,7 +597,8 @@ hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, co
                                  router_lg_bytes(32 * TT, p.Epad)) + 4LL * p.k * p.Epad;         \
     if ((err = set_lds(router_bf16_kernel<TT, EW, S>, lds)) != hipSuccess) return err;           \
     hipLaunchKernelGGL((router_bf16_kernel<TT, EW, S>), dim3(p.NB), dim3(256), lds, s, xb, planes, \
-                       flags, bias, T, d, p.E, p.Epad, p.k, expert_idx, gate, hist, p.NB, psum); \
+                       flags, bias, T, d, p.E, p.Epad, p.k, expert_idx, gate, hist, p.NB, psum,   \
+                       logits);                                                                  \
   } while (0)
     if (p.Epad <= 128) {
       if (p.TB == 32) MOE_ROUTER_BF16(1, 1, 4);
@@ -615,7 +620,7 @@ hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, co
                         4LL * p.k * 4 * N;                                                       \
     if ((err = set_lds(router_f32_kernel<N>, lds)) != hipSuccess) return err;                    \
     hipLaunchKernelGGL(router_f32_kernel<N>, dim3(p.NB), dim3(256), lds, s, xf, w_r, bias, T, d, \
-                       p.E, p.k, expert_idx, gate, hist, p.NB, psum, p.Epad);                   \
+                       p.E, p.k, expert_idx, gate, hist, p.NB, psum, p.Epad, logits);           \
   } while (0)
     if (p.E <= 32) MOE_ROUTER_F32(8);
     else if (p.E <= 64) MOE_ROUTER_F32(16);

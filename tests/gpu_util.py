@@ -129,6 +129,23 @@ class Dev:
         torch.cuda.synchronize()
         return idx, gate, aux.cpu().numpy()
 
+    def run_backward(self, dy_host, with_dbias=True):
+        """moe_forward, then moe_backward for the upstream gradient dy (stored dtype)."""
+        wl, cfg = self.wl, self.cfg
+        y = self.new((wl.T, wl.d_model), elem_dtype(wl))
+        moe.forward(cfg, self.x, self.w_r, self.bias, self.group_id, self.w1, self.w2, y, self.ws)
+        dy = to_dev(dy_host)
+        out = {"dx": self.new((wl.T, wl.d_model), elem_dtype(wl)),
+               "dw1": self.new((wl.E, wl.d_ff, wl.d_model), elem_dtype(wl)),
+               "dw2": self.new((wl.E, wl.d_model, wl.d_ff), elem_dtype(wl)),
+               "dw_r": self.new((wl.E, wl.d_model), torch.float32) if wl.route == "topk" else None,
+               "dbias": self.new((wl.E,), torch.float32) if (with_dbias and wl.route == "topk") else None}
+        bws = moe.alloc_backward_workspace(cfg)
+        moe.backward(cfg, self.x, self.w_r, self.bias, self.w1, self.w2, dy, out["dx"], out["dw_r"],
+                     out["dbias"], out["dw1"], out["dw2"], self.ws, bws)
+        torch.cuda.synchronize()
+        return out
+
     def run_forward(self):
         wl = self.wl
         y = self.new((wl.T, wl.d_model), elem_dtype(wl))
@@ -164,6 +181,26 @@ def check_router_aux(wl, inputs, idx, gate, aux, alpha=1e-2, label=""):
     err = abs(float(aux[0]) - loss_ref) / loss_ref
     assert err <= aux_tol(E), f"{label} loss rel err {err:.3g} (gpu {aux[0]}, oracle {loss_ref})"
     return err
+
+
+def make_dy(wl, seed=11):
+    """Seeded upstream gradient in the layer's storage dtype (N(0, 1))."""
+    g = np.random.default_rng(seed).standard_normal((wl.T, wl.d_model)).astype(np.float32)
+    return W.f32_to_bf16_bits(g) if wl.dtype == "bf16" else g
+
+
+def check_backward(wl, got, ref, label=""):
+    """Gradients of moe_backward against the oracle's float64 backward (normwise
+    max-abs-rel within the layer's output tolerance)."""
+    tol = out_tol(wl)
+    errs = {}
+    for key in ("dx", "dw1", "dw2", "dw_r", "dbias"):
+        if got.get(key) is None or ref.get(key) is None:
+            continue
+        g = to_host_f64(got[key])
+        errs[key] = max_abs_rel(g, ref[key])
+        assert errs[key] <= tol, f"{label} {key} max-abs-rel {errs[key]:.3g} > {tol}"
+    return errs
 
 
 def check_routing(wl, got, ref, label=""):

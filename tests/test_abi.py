@@ -225,6 +225,29 @@ def test_router_aux_rejections():
         _lib.MOE_ERR_ARG
 
 
+def test_backward_rejections():
+    lib = moe.load()
+    ok = ctypes.c_void_p(0x100000)
+    cfg = _cfg()
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg)) > 0
+    args = [ok, ok, None, ok, ok, ok, ok, ok, None, ok, ok, ok, ok, None]
+    for i, name in [(5, "dy"), (6, "dx"), (7, "dw_r"), (9, "dw1"), (10, "dw2"), (12, "bws")]:
+        a = list(args)
+        a[i] = None
+        assert lib.moe_backward(ctypes.byref(cfg), *a) == _lib.MOE_ERR_ARG, name
+        assert lib.moe_last_error().decode().startswith(name + " "), name
+    # random routed experts: no router weight or its gradient needed
+    rre = _cfg(route=1, k=1, n_groups=4)
+    a = list(args)
+    a[1] = None
+    a[7] = None
+    a[12] = None   # fails on the scratch buffer, after every router argument was accepted
+    assert lib.moe_backward(ctypes.byref(rre), *a) == _lib.MOE_ERR_ARG
+    assert lib.moe_last_error().decode().startswith("bws")
+    bad = _cfg(k=0)
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(bad)) == _lib.MOE_ERR_ARG
+
+
 def test_binding_raises_on_error():
     cfg = moe.make_config(10, 64, 64, 4, 5, 1.0)
     with pytest.raises(moe.MoeError, match="k must be"):

@@ -13,7 +13,8 @@ import pytest
 
 import moe_workloads as W
 import oracle
-from gpu_util import Dev, check_layer_output, check_router_aux, check_routing, to_host_f64
+from gpu_util import (Dev, check_backward, check_layer_output, check_router_aux, check_routing,
+                      make_dy, to_host_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +85,21 @@ def test_full_size_router_aux(name):
     idx, gate, aux = dev.run_router_aux(alpha=1e-2)
     err = check_router_aux(wl, inputs, idx, gate, aux, 1e-2, name)
     print(f"[gpu] full router aux {name}: loss {aux[0]:.6g}, rel err {err:.3g}", flush=True)
+
+
+def test_full_size_backward_switch_base():
+    """moe_backward on the Switch-Base layer against the oracle's float64 backward (all
+    gradients, every token and expert)."""
+    wl = W.WORKLOADS["switch_base_bf16"]
+    t0 = time.time()
+    print("[gpu] full backward switch_base_bf16: inputs", flush=True)
+    inputs = W.make_inputs(wl)
+    dev = Dev(wl, inputs)
+    dy = make_dy(wl)
+    got = dev.run_backward(dy)
+    print(f"[gpu] full backward switch_base_bf16: oracle ({time.time() - t0:.1f}s)", flush=True)
+    fwd = oracle.forward(wl, inputs)
+    ref = oracle.backward(wl, inputs, fwd, oracle.as_f64(dy))
+    errs = check_backward(wl, got, ref, "switch_base_bf16")
+    print("[gpu] full backward switch_base_bf16: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items())
+          + f" ({time.time() - t0:.1f}s)", flush=True)
