@@ -22,12 +22,12 @@
 // token-major operands of the weight gradients, whose contraction runs over
 // the tokens of an expert) is staged as [k][row] with 16-byte stores and read
 // as eight 2-byte values per fragment.  Register-staged double buffering,
-// 32-k steps, v_mfma_f32_32x32x16_bf16 with float32 accumulation, D = B . A^T
+// 64-k steps (32 for the token-contracted ones), v_mfma_f32_32x32x16_bf16 with float32 accumulation, D = B . A^T
 // so each lane stores four consecutive output columns.  act' is applied in the
 // dH epilogue (from the hidden activation for ReLU, from the recomputed
 // pre-activation for GELU).  The router products (K = E or K = T) and the
 // float32 layers use a float32 FMA tile kernel with the same orientation
-// flags; the token-contracted router weight gradient is split over 16 token
+// flags; the token-contracted router weight gradient is split over 64 token
 // ranges and the ranges are added in order (deterministic, no atomics).
 #include "moe_common.h"
 #include "moe_internal.h"
@@ -184,7 +184,6 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(
 // at the output position (ACT 0: z is the hidden activation, act' = z > 0;
 // ACT 1: z is the pre-activation, act' = GELU derivative).
 // ---------------------------------------------------------------------------
-constexpr int GBK2 = 32;
 
 __device__ __forceinline__ float gelu_grad(float z) {
   const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
@@ -192,26 +191,30 @@ __device__ __forceinline__ float gelu_grad(float z) {
   return fmaf(z, pdf, cdf);
 }
 
-template <int ROWS, bool KC>
+template <int ROWS, bool KC, int BK>
 struct OpTile {
-  // LDS elements per buffer: [ROWS][GBK2 + 8] (k-contiguous) or [GBK2][ROWS + 8]
-  static constexpr int kPitch = KC ? GBK2 + 8 : ROWS + 8;
-  static constexpr int kElems = KC ? ROWS * (GBK2 + 8) : GBK2 * (ROWS + 8);
-  static constexpr int kChunks = ROWS * GBK2 / 8;  // 16-byte chunks per tile
+  // LDS elements per buffer: [ROWS][BK + 8] (k-contiguous) or [BK][ROWS + 8]
+  static constexpr int kPitch = KC ? BK + 8 : ROWS + 8;
+  static constexpr int kElems = KC ? ROWS * (BK + 8) : BK * (ROWS + 8);
+  static constexpr int kChunks = ROWS * BK / 8;  // 16-byte chunks per tile
 };
 
-template <int BM, int BN, bool AKC, bool BKC, int EPI, int ACT>
+template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI, int ACT>
 __global__ __launch_bounds__(256) void bgemm_kernel(
     const bf16_t* __restrict__ A, int64_t sAe, int lda, const bf16_t* __restrict__ B, int64_t sBe,
     int ldb, bf16_t* __restrict__ out, int64_t sOe, int ldo, const bf16_t* __restrict__ aux,
     const int32_t* __restrict__ count, int64_t C, int M, int N, int K, bool m_is_count) {
-  using TA = OpTile<BM, AKC>;
-  using TBt = OpTile<BN, BKC>;
+  using TA = OpTile<BM, AKC, BK>;
+  using TBt = OpTile<BN, BKC, BK>;
   static_assert(TA::kChunks % 256 == 0 && TBt::kChunks % 256 == 0, "chunk split");
   constexpr int CA = TA::kChunks / 256, CB = TBt::kChunks / 256;
   constexpr int TM = BM / 64, TN = BN / 64;  // 32-row MFMA tiles per wave (2 x 2 waves)
-  __shared__ __align__(16) bf16_t la[2][TA::kElems];
-  __shared__ __align__(16) bf16_t lb[2][TBt::kElems];
+  // operand double buffers, reused after the k loop as the output staging tile
+  constexpr int OP = BN + 8;  // staging row pitch (elements)
+  constexpr int kSmem = 2 * (TA::kElems + TBt::kElems) > BM * OP ? 2 * (TA::kElems + TBt::kElems) : BM * OP;
+  __shared__ __align__(16) bf16_t smem_[kSmem];
+  bf16_t (*la)[TA::kElems] = reinterpret_cast<bf16_t (*)[TA::kElems]>(smem_);
+  bf16_t (*lb)[TBt::kElems] = reinterpret_cast<bf16_t (*)[TBt::kElems]>(smem_ + 2 * TA::kElems);
 
   const int e = blockIdx.z;
   int64_t cnt = count[e];
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
       const int q = tid + 256 * i;
       u32x4 v = {0u, 0u, 0u, 0u};
       if constexpr (AKC) {
-        const int r = q / (GBK2 / 8), kc = q % (GBK2 / 8);
+        const int r = q / (BK / 8), kc = q % (BK / 8);
         const int m = m0 + r, kk = k0 + kc * 8;
         if (m < M && kk < Kv) v = *reinterpret_cast<const u32x4*>(Ae + static_cast<int64_t>(m) * lda + kk);
       } else {
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
       const int q = tid + 256 * i;
       u32x4 v = {0u, 0u, 0u, 0u};
       if constexpr (BKC) {
-        const int r = q / (GBK2 / 8), kc = q % (GBK2 / 8);
+        const int r = q / (BK / 8), kc = q % (BK / 8);
         const int n = n0 + r, kk = k0 + kc * 8;
         if (n < N && kk < Kv) v = *reinterpret_cast<const u32x4*>(Be + static_cast<int64_t>(n) * ldb + kk);
       } else {
@@ -263,14 +266,14 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       const int q = tid + 256 * i;
-      const int idx = AKC ? (q / (GBK2 / 8)) * TA::kPitch + (q % (GBK2 / 8)) * 8
+      const int idx = AKC ? (q / (BK / 8)) * TA::kPitch + (q % (BK / 8)) * 8
                           : (q / (BM / 8)) * TA::kPitch + (q % (BM / 8)) * 8;
       *reinterpret_cast<u32x4*>(&la[buf][idx]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       const int q = tid + 256 * i;
-      const int idx = BKC ? (q / (GBK2 / 8)) * TBt::kPitch + (q % (GBK2 / 8)) * 8
+      const int idx = BKC ? (q / (BK / 8)) * TBt::kPitch + (q % (BK / 8)) * 8
                           : (q / (BN / 8)) * TBt::kPitch + (q % (BN / 8)) * 8;
       *reinterpret_cast<u32x4*>(&lb[buf][idx]) = rb[i];
     }
@@ -294,16 +297,16 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
 
-  const int nk = (Kv + GBK2 - 1) / GBK2;
+  const int nk = (Kv + BK - 1) / BK;
   if (nk > 0) {
     load(0);
     store(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       const int buf = kt & 1;
-      if (kt + 1 < nk) load((kt + 1) * GBK2);
+      if (kt + 1 < nk) load((kt + 1) * BK);
 #pragma unroll
-      for (int j = 0; j < GBK2 / 16; ++j) {
+      for (int j = 0; j < BK / 16; ++j) {
         bf16x8 fa[TM], fb[TN];
 #pragma unroll
         for (int t = 0; t < TM; ++t) fa[t] = frag(la[buf], AKC, TA::kPitch, (wm * TM + t) * 32 + fr, j);
@@ -319,36 +322,52 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
       __syncthreads();
     }
   }
-  // D[n][m]: lane holds m = fr and n = 8 * (r / 4) + 4 * half + r % 4 of each 32 x 32 tile
+  // D[n][m]: lane holds m = fr and n = 8 * (r / 4) + 4 * half + r % 4 of each 32 x 32 tile.
+  // The tile goes through LDS (the operand buffers are free after the last
+  // barrier of the k loop), then out with 16-byte stores, four 256-byte row
+  // segments per wave instruction.
   bf16_t* Oe = out + e * sOe;
   const bf16_t* Ze = aux ? aux + e * sOe : nullptr;
+  bf16_t* st = smem_;  // [BM][OP]
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
-    const int m = m0 + (wm * TM + t) * 32 + fr;
-    if (m >= Mv) continue;
+    const int ml = (wm * TM + t) * 32 + fr;
+    const int m = m0 + ml;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
-      const int nt0 = n0 + (wn * TN + i) * 32;
-      if (nt0 >= N) continue;  // N % 32 == 0
+      const int nl0 = (wn * TN + i) * 32;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = nt0 + 8 * q + 4 * half;
+        const int nl = nl0 + 8 * q + 4 * half;
         float v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) v[u] = acc[i][t][4 * q + u];
         if constexpr (EPI == 1) {
-          const uint2 zz = *reinterpret_cast<const uint2*>(Ze + static_cast<int64_t>(m) * ldo + n);
-          const float z[4] = {__uint_as_float(zz.x << 16), __uint_as_float(zz.x & 0xFFFF0000u),
-                              __uint_as_float(zz.y << 16), __uint_as_float(zz.y & 0xFFFF0000u)};
+          if (m < Mv && n0 + nl < N) {
+            const uint2 zz = *reinterpret_cast<const uint2*>(Ze + static_cast<int64_t>(m) * ldo + n0 + nl);
+            const float z[4] = {__uint_as_float(zz.x << 16), __uint_as_float(zz.x & 0xFFFF0000u),
+                                __uint_as_float(zz.y << 16), __uint_as_float(zz.y & 0xFFFF0000u)};
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] *= ACT == 0 ? (z[u] > 0.f ? 1.f : 0.f) : gelu_grad(z[u]);
+            for (int u = 0; u < 4; ++u) v[u] *= ACT == 0 ? (z[u] > 0.f ? 1.f : 0.f) : gelu_grad(z[u]);
+          }
         }
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);
         w.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(Oe + static_cast<int64_t>(m) * ldo + n) = w;
+        *reinterpret_cast<uint2*>(st + ml * OP + nl) = w;
       }
     }
+  }
+  __syncthreads();
+  constexpr int CPRow = BN / 8;  // 16-byte chunks per row
+#pragma unroll
+  for (int it = 0; it < BM * CPRow / 256; ++it) {
+    const int q = it * 256 + tid;
+    const int ml = q / CPRow, c = q % CPRow;
+    const int m = m0 + ml, n = n0 + c * 8;
+    if (m < Mv && n < N)
+      *reinterpret_cast<u32x4*>(Oe + static_cast<int64_t>(m) * ldo + n) =
+          *reinterpret_cast<const u32x4*>(st + ml * OP + c * 8);
   }
 }
 
@@ -486,7 +505,7 @@ __global__ __launch_bounds__(64) void bwd_bias_kernel(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int BM, int BN, bool AKC, bool BKC, int EPI, int ACT>
+template <int BM, int BN, int BK, bool AKC, bool BKC, int EPI, int ACT>
 static hipError_t run_bgemm(const Plan& p, const bf16_t* A, int64_t sAe, int lda, const bf16_t* B,
                             int64_t sBe, int ldb, bf16_t* out, int64_t sOe, int ldo,
                             const bf16_t* aux, const int32_t* count, int M, int N, int K,
@@ -494,7 +513,7 @@ static hipError_t run_bgemm(const Plan& p, const bf16_t* A, int64_t sAe, int lda
   const int mtiles = ((m_is_count ? static_cast<int>(p.C) : M) + BM - 1) / BM;
   const dim3 grid((N + BN - 1) / BN, mtiles, p.E);
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  hipLaunchKernelGGL((bgemm_kernel<BM, BN, AKC, BKC, EPI, ACT>), grid, dim3(256), 0, s, A, sAe, lda, B,
+  hipLaunchKernelGGL((bgemm_kernel<BM, BN, BK, AKC, BKC, EPI, ACT>), grid, dim3(256), 0, s, A, sAe, lda, B,
                      sBe, ldb, out, sOe, ldo, aux, count, p.C, M, N, K, m_is_count);
   return hipGetLastError();
 }
@@ -538,19 +557,19 @@ hipError_t expert_backward<bf16_t>(const Plan& p, const bf16_t* x_e, const bf16_
   const bf16_t* z = p.act == 1 ? zbuf : hidden;
   // dZ[s][f] = sum_d dy_e[s][d] w2[d][f] * act'(Z)   (A = dy_e k-contiguous, B = w2 [k=d][n=f])
   if (p.act == 0)
-    MOE_TRY((run_bgemm<64, 128, true, false, 1, 0>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
+    MOE_TRY((run_bgemm<64, 128, 64, true, false, 1, 0>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
                                                     f, d, true, s)));
   else
-    MOE_TRY((run_bgemm<64, 128, true, false, 1, 1>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
+    MOE_TRY((run_bgemm<64, 128, 64, true, false, 1, 1>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
                                                     f, d, true, s)));
   // dx_e[s][d] = sum_f dZ[s][f] w1[f][d]   (B = w1 [k=f][n=d])
-  MOE_TRY((run_bgemm<64, 128, true, false, 0, 0>(p, dz, sH, f, w1, sW, d, dx_e, sX, d, nullptr, count,
+  MOE_TRY((run_bgemm<64, 128, 64, true, false, 0, 0>(p, dz, sH, f, w1, sW, d, dx_e, sX, d, nullptr, count,
                                                   Ci, d, f, true, s)));
   // dw2[d][f] = sum_s dy_e[s][d] H[s][f]   (A = dy_e [k=s][m=d], B = H [k=s][n=f])
-  MOE_TRY((run_bgemm<128, 128, false, false, 0, 0>(p, dy_e, sX, d, hidden, sH, f, dw2, sW, f, nullptr,
+  MOE_TRY((run_bgemm<128, 128, 32, false, false, 0, 0>(p, dy_e, sX, d, hidden, sH, f, dw2, sW, f, nullptr,
                                                     count, d, f, 0, false, s)));
   // dw1[f][d] = sum_s dZ[s][f] x_e[s][d]
-  MOE_TRY((run_bgemm<128, 128, false, false, 0, 0>(p, dz, sH, f, x_e, sX, d, dw1, sW, d, nullptr, count,
+  MOE_TRY((run_bgemm<128, 128, 32, false, false, 0, 0>(p, dz, sH, f, x_e, sX, d, dw1, sW, d, nullptr, count,
                                                     f, d, 0, false, s)));
   return hipSuccess;
 }

@@ -68,7 +68,7 @@ hipError_t launch_expert_up_act(const Plan& p, const void* x_e, const int32_t* e
                                 const void* w1, void* out, int act, hipStream_t s);
 
 // backward.hip
-constexpr int kBwdSplit = 16;  // token ranges of the router weight gradient
+constexpr int kBwdSplit = 64;  // token ranges of the router weight gradient
 struct BwdArgs {
   // inputs and outputs of the call
   const void* x;
