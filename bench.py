@@ -197,6 +197,9 @@ def main():
     bws = moe.alloc_backward_workspace(cfg, dev)
     kern_us["backward"] = timed(lambda: moe.backward(cfg, x, w_r, bias, w1, w2, dy_t, dx_t, dwr_t, dbias_t,
                                                      dw1_t, dw2_t, ws, bws, stream), max(2, R // 2))
+    nc_t = torch.empty(2, dtype=torch.float32, device=dev)
+    kern_us["sparse_clip"] = timed(lambda: moe.sparse_clip(cfg, dwr_t, dbias_t, dw1_t, dw2_t, 1e30, nc_t, bws,
+                                                           stream), max(2, R // 2))
     del dw1_t, dw2_t, bws
     try:  # the single-launch FFN, where its shape conditions hold
         kern_us["ffn_fused"] = timed(lambda: moe.expert_ffn_fused(cfg, x_e, cnt_t, w1, w2, y_e, stream), R)

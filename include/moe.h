@@ -240,6 +240,19 @@ int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const f
                  const void* w1, const void* w2, const void* dy, void* dx, float* dw_r,
                  float* dbias, void* dw1, void* dw2, void* ws, void* bws, void* stream);
 
+/* SparseClip (TorchScale review, methodology): gradient clipping for sparse MoE
+ * models whose norm re-weights the MoE gradients by kappa = 1/sqrt(E) against the
+ * dense ones, norm = ||(g_dense, kappa g_moe)||_2.  Here the dense gradients are
+ * the router's (dw_r, dbias: each may be NULL) and the MoE gradients the
+ * experts' (dw1, dw2, dtype, as moe_backward writes them).  Every gradient is
+ * multiplied in place by coef = min(1, max_norm / (norm + 1e-6)) (float32
+ * product, rounded to the gradient's dtype).
+ *   norm_coef  [2] float32 out (device): norm, coef
+ *   bws        the backward workspace (moe_backward_workspace_bytes).
+ * Sums of squares run in float64 in a fixed order (identical bits on repeat). */
+int moe_sparse_clip(const moe_config* cfg, float* dw_r, float* dbias, void* dw1, void* dw2,
+                    double max_norm, float* norm_coef, void* bws, void* stream);
+
 /* Message of the last non-OK status on this thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -467,3 +467,28 @@ def backward(wl, inputs, fwd: dict, dy: np.ndarray,
         dw_r = dh.T @ x
         dbias = dh.sum(axis=0) if inputs.get("bias") is not None else None
     return dict(dx=dx, dw1=dw1, dw2=dw2, dw_r=dw_r, dbias=dbias, dgate=dgate)
+
+
+# ---------------------------------------------------------------------------
+# NEXT: SparseClip gradient clipping
+# ---------------------------------------------------------------------------
+
+
+def sparse_clip(grads: dict, E: int, max_norm: float) -> tuple:
+    """SparseClip ([X-MoE] TorchScale review, methodology): gradient clipping whose norm
+    re-weights the MoE (expert) gradients by kappa = 1/sqrt(E), balancing them against the
+    dense ones: norm = ||(g_dense, kappa * g_moe)||_2.
+
+    Reading taken where the page is silent: the dense gradients of this layer are the
+    router's (dw_r, dbias), the MoE gradients the experts' (dw1, dw2); the clipping
+    coefficient is min(1, max_norm / (norm + 1e-6)) applied to every gradient, the usual
+    clip-by-global-norm rule.  float64.  Returns (clipped gradients, norm, coefficient).
+    """
+    dense = [g for g in (grads.get("dw_r"), grads.get("dbias")) if g is not None]
+    moe = [grads["dw1"], grads["dw2"]]
+    sq_dense = sum(float(np.sum(np.asarray(g, np.float64) ** 2)) for g in dense)
+    sq_moe = sum(float(np.sum(np.asarray(g, np.float64) ** 2)) for g in moe)
+    norm = math.sqrt(sq_dense + sq_moe / E)
+    coef = min(1.0, max_norm / (norm + 1e-6))
+    out = {k: (None if v is None else np.asarray(v, np.float64) * coef) for k, v in grads.items()}
+    return out, norm, coef

@@ -20,7 +20,7 @@ from ._lib import ACT, DTYPE, EXPORTS, REGION, ROUTE, MoeConfig, load  # noqa: F
 __all__ = ["MoeConfig", "MoeError", "make_config", "config_for", "capacity", "workspace_bytes",
            "workspace_offset", "alloc_workspace", "workspace_view", "router", "router_aux", "dispatch",
            "expert_ffn", "expert_ffn_fused", "expert_up", "expert_down", "combine", "forward", "backward_workspace_bytes", "alloc_backward_workspace",
-           "backward", "version", "load"]
+           "backward", "sparse_clip", "version", "load"]
 
 
 class MoeError(RuntimeError):
@@ -168,6 +168,11 @@ def backward(cfg, x, w_r, bias, w1, w2, dy, dx, dw_r, dbias, dw1, dw2, ws, bws, 
     _status(load().moe_backward(ctypes.byref(cfg), _ptr(x), _ptr(w_r), _ptr(bias), _ptr(w1), _ptr(w2),
                                 _ptr(dy), _ptr(dx), _ptr(dw_r), _ptr(dbias), _ptr(dw1), _ptr(dw2),
                                 _ptr(ws), _ptr(bws), _stream(stream)))
+
+
+def sparse_clip(cfg, dw_r, dbias, dw1, dw2, max_norm, norm_coef, bws, stream=None) -> None:
+    _status(load().moe_sparse_clip(ctypes.byref(cfg), _ptr(dw_r), _ptr(dbias), _ptr(dw1), _ptr(dw2),
+                                   float(max_norm), _ptr(norm_coef), _ptr(bws), _stream(stream)))
 
 
 def forward(cfg, x, w_r, bias, group_id, w1, w2, y, ws, stream=None) -> None:

@@ -15,7 +15,7 @@ REGION = {"expert_idx": 0, "gate": 1, "slot": 2, "expert_count": 3, "slot_token"
           "x_e": 5, "hidden": 6, "y_e": 7}
 
 EXPORTS = ["moe_capacity", "moe_workspace_bytes", "moe_workspace_offset", "moe_router", "moe_router_aux",
-           "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_fused", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_backward_workspace_bytes", "moe_backward", "moe_last_error",
+           "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_fused", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_backward_workspace_bytes", "moe_backward", "moe_sparse_clip", "moe_last_error",
            "moe_version"]
 
 
@@ -78,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.moe_backward_workspace_bytes.restype = i64
     lib.moe_backward.argtypes = [cfgp] + [P] * 13
     lib.moe_backward.restype = ctypes.c_int
+    lib.moe_sparse_clip.argtypes = [cfgp, P, P, P, P, ctypes.c_double, P, P, P]
+    lib.moe_sparse_clip.restype = ctypes.c_int
     lib.moe_last_error.argtypes = []
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_version.argtypes = []

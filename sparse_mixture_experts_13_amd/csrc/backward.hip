@@ -671,3 +671,101 @@ hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t s) {
 #undef MOE_TRY
 
 }  // namespace moe
+
+// ---------------------------------------------------------------------------
+// SparseClip (TorchScale review, methodology): clipping norm with the MoE
+// (expert) gradients re-weighted by kappa = 1/sqrt(E),
+//   norm = sqrt(|g_dense|^2 + |g_moe|^2 / E),  coef = min(1, max_norm / (norm + 1e-6)),
+// every gradient multiplied by coef.  Sums of squares in float64: block b of a
+// launch takes the b-th contiguous range of the array; one block adds the
+// partials in order.  Dense = router gradients, MoE = expert weight gradients.
+// ---------------------------------------------------------------------------
+namespace moe {
+
+constexpr int kClipBlocks = 512;
+
+template <typename T>
+__global__ __launch_bounds__(256) void clip_sumsq_kernel(const T* __restrict__ p, int64_t n,
+                                                         double* __restrict__ part) {
+  __shared__ double red[256];
+  const int64_t b0 = n * blockIdx.x / gridDim.x, b1 = n * (blockIdx.x + 1) / gridDim.x;
+  double acc = 0.0;
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += 256) {
+    const double v = static_cast<double>(ld_f32(p + i));
+    acc = fma(v, v, acc);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// part: [4][kClipBlocks] (dw_r, dbias, dw1, dw2); out: norm, coef (float).
+// Thread t adds partials 2t and 2t + 1 of each array, then a fixed tree.
+__global__ __launch_bounds__(256) void clip_coef_kernel(const double* __restrict__ part, int E,
+                                                        double max_norm, float* __restrict__ out) {
+  static_assert(kClipBlocks == 512, "two partials per thread");
+  __shared__ double red[4][256];
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) red[a][t] = part[a * kClipBlocks + 2 * t] + part[a * kClipBlocks + 2 * t + 1];
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) red[a][t] += red[a][t + w];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    const double norm = sqrt((red[0][0] + red[1][0]) + (red[2][0] + red[3][0]) / E);
+    const double coef = fmin(1.0, max_norm / (norm + 1e-6));
+    out[0] = static_cast<float>(norm);
+    out[1] = static_cast<float>(coef);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void clip_scale_kernel(T* __restrict__ p, int64_t n,
+                                                         const float* __restrict__ nc) {
+  const float c = nc[1];
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    st_f32(p + i, ld_f32(p + i) * c);
+}
+
+template <typename T>
+static hipError_t clip_typed(const Plan& p, float* dw_r, float* dbias, T* dw1, T* dw2,
+                             double max_norm, float* nc, double* part, hipStream_t s) {
+  const int64_t nw = int64_t(p.E) * p.d * p.f;
+  const int64_t nr = dw_r ? int64_t(p.E) * p.d : 0, nb = dbias ? p.E : 0;
+  // empty arrays still write their (zero) partials
+  hipLaunchKernelGGL(clip_sumsq_kernel<float>, dim3(kClipBlocks), dim3(256), 0, s, dw_r, nr, part);
+  hipLaunchKernelGGL(clip_sumsq_kernel<float>, dim3(kClipBlocks), dim3(256), 0, s, dbias, nb,
+                     part + kClipBlocks);
+  hipLaunchKernelGGL(clip_sumsq_kernel<T>, dim3(kClipBlocks), dim3(256), 0, s, dw1, nw,
+                     part + 2 * kClipBlocks);
+  hipLaunchKernelGGL(clip_sumsq_kernel<T>, dim3(kClipBlocks), dim3(256), 0, s, dw2, nw,
+                     part + 3 * kClipBlocks);
+  hipLaunchKernelGGL(clip_coef_kernel, dim3(1), dim3(256), 0, s, part, p.E, max_norm, nc);
+  const unsigned g = 2048;
+  if (nr) hipLaunchKernelGGL(clip_scale_kernel<float>, dim3(g), dim3(256), 0, s, dw_r, nr, nc);
+  if (nb) hipLaunchKernelGGL(clip_scale_kernel<float>, dim3(1), dim3(256), 0, s, dbias, nb, nc);
+  hipLaunchKernelGGL(clip_scale_kernel<T>, dim3(g), dim3(256), 0, s, dw1, nw, nc);
+  hipLaunchKernelGGL(clip_scale_kernel<T>, dim3(g), dim3(256), 0, s, dw2, nw, nc);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_clip(const Plan& p, float* dw_r, float* dbias, void* dw1, void* dw2,
+                              double max_norm, float* norm_coef, void* part, hipStream_t s) {
+  double* pp = static_cast<double*>(part);
+  return p.dtype == 1 ? clip_typed<bf16_t>(p, dw_r, dbias, static_cast<bf16_t*>(dw1),
+                                           static_cast<bf16_t*>(dw2), max_norm, norm_coef, pp, s)
+                      : clip_typed<float>(p, dw_r, dbias, static_cast<float*>(dw1),
+                                          static_cast<float*>(dw2), max_norm, norm_coef, pp, s);
+}
+
+}  // namespace moe

@@ -130,7 +130,7 @@ void make_plan(const moe_config* cfg, moe::Plan& p) {
 
 // Backward scratch (second workspace): byte offsets of its buffers.
 struct BwdLayout {
-  int64_t idx, gate, dgate, dy_e, zbuf, dz, dx_e, dh, dx_r, dwr_part, total;
+  int64_t idx, gate, dgate, dy_e, zbuf, dz, dx_e, dh, dx_r, dwr_part, clip, total;
 };
 
 void bwd_layout(const moe::Plan& p, BwdLayout& L) {
@@ -152,6 +152,7 @@ void bwd_layout(const moe::Plan& p, BwdLayout& L) {
   L.dh = take(topk ? p.T * p.Epad * 4 : 0);
   L.dx_r = take(topk ? p.T * p.d * 4 : 0);
   L.dwr_part = take(topk ? int64_t(moe::kBwdSplit) * p.E * p.d * 4 : 0);
+  L.clip = take(moe::kClipScratchBytes);
   L.total = off;
 }
 
@@ -470,6 +471,26 @@ int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const f
   a.dx_r = reinterpret_cast<float*>(bb + L.dx_r);
   a.dwr_part = reinterpret_cast<float*>(bb + L.dwr_part);
   MOE_HIP(moe::launch_backward(p, a, static_cast<hipStream_t>(stream)), "backward");
+  return MOE_OK;
+}
+
+int moe_sparse_clip(const moe_config* cfg, float* dw_r, float* dbias, void* dw1, void* dw2,
+                    double max_norm, float* norm_coef, void* bws, void* stream) {
+  MOE_CHECK(validate(cfg));
+  if (!(max_norm > 0.0) || !std::isfinite(max_norm))
+    return fail(MOE_ERR_ARG, "max_norm must be finite and > 0");
+  moe::Plan p;
+  make_plan(cfg, p);
+  BwdLayout L;
+  bwd_layout(p, L);
+  const int64_t wbytes = int64_t(p.E) * p.d * p.f * p.elem;
+  MOE_CHECK(need(dw1, wbytes, "dw1"));
+  MOE_CHECK(need(dw2, wbytes, "dw2"));
+  MOE_CHECK(need(norm_coef, 8, "norm_coef"));
+  MOE_CHECK(need(bws, L.total, "bws"));
+  MOE_HIP(moe::launch_sparse_clip(p, dw_r, dbias, dw1, dw2, max_norm, norm_coef,
+                                  static_cast<char*>(bws) + L.clip, static_cast<hipStream_t>(stream)),
+          "sparse clip");
   return MOE_OK;
 }
 

@@ -104,6 +104,10 @@ struct BwdArgs {
   float* dwr_part;
 };
 hipError_t launch_backward(const Plan& p, const BwdArgs& a, hipStream_t s);
+// SparseClip in place; norm_coef = [norm, coef] (device floats); part: 4 x 512 doubles
+constexpr int64_t kClipScratchBytes = 4 * 512 * 8;
+hipError_t launch_sparse_clip(const Plan& p, float* dw_r, float* dbias, void* dw1, void* dw2,
+                              double max_norm, float* norm_coef, void* part, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const Plan& p, const void* y_e, const int32_t* expert_idx,

@@ -555,3 +555,36 @@ def check_backward_rre_no_router_grad(rng):
         (yv * torch.tensor(dy[t:t + 1])).sum().backward()
         dx_ref[t] = xt.grad.numpy()[0]
     np.testing.assert_allclose(g["dx"], dx_ref, rtol=1e-12, atol=1e-12)
+
+
+def check_sparse_clip(rng):
+    import torch
+    # E = 1: kappa = 1, the norm is the plain global 2-norm; torch's clip_grad_norm_ agrees
+    g = {"dw_r": rng.normal(size=(1, 5)), "dbias": rng.normal(size=1),
+         "dw1": rng.normal(size=(1, 6, 5)), "dw2": rng.normal(size=(1, 5, 6))}
+    for max_norm in (0.5, 1e6):
+        out, norm, coef = O.sparse_clip(g, 1, max_norm)
+        ts = [torch.tensor(g[k], requires_grad=True) for k in ("dw_r", "dbias", "dw1", "dw2")]
+        for t, k in zip(ts, ("dw_r", "dbias", "dw1", "dw2")):
+            t.grad = torch.tensor(g[k])
+        tn = float(torch.nn.utils.clip_grad_norm_(ts, max_norm))
+        assert abs(norm - tn) <= 1e-12 * tn
+        for t, k in zip(ts, ("dw_r", "dbias", "dw1", "dw2")):
+            np.testing.assert_allclose(out[k], t.grad.numpy(), rtol=1e-12, atol=0)
+        assert coef == (1.0 if max_norm > norm else coef) and coef <= 1.0
+    # kappa = 1/sqrt(E): scaling every expert gradient by sqrt(E) and the dense ones by 1
+    # gives the norm of the unscaled gradients with E = 1
+    E = 16
+    g2 = {"dw_r": rng.normal(size=(E, 4)), "dbias": None,
+          "dw1": rng.normal(size=(E, 3, 4)), "dw2": rng.normal(size=(E, 4, 3))}
+    _, n1, _ = O.sparse_clip(g2, 1, 1.0)
+    g3 = dict(g2, dw1=g2["dw1"] * math.sqrt(E), dw2=g2["dw2"] * math.sqrt(E))
+    _, n2, _ = O.sparse_clip(g3, E, 1.0)
+    assert abs(n1 - n2) <= 1e-12 * n1
+    # hand-worked: dense (3, 4) -> 25; experts all 2, 8 values, E = 4: 8*4/4 = 8 -> norm sqrt(33)
+    g4 = {"dw_r": np.array([[3.0, 4.0]]), "dbias": None, "dw1": np.full((4, 1, 1), 2.0),
+          "dw2": np.full((4, 1, 1), 2.0)}
+    out, norm, coef = O.sparse_clip(g4, 4, 1.0)
+    assert abs(norm - math.sqrt(33.0)) < 1e-12
+    assert abs(coef - 1.0 / (math.sqrt(33.0) + 1e-6)) < 1e-15
+    np.testing.assert_allclose(out["dw_r"], g4["dw_r"] * coef, rtol=1e-15)

@@ -248,6 +248,20 @@ def test_backward_rejections():
     assert lib.moe_backward_workspace_bytes(ctypes.byref(bad)) == _lib.MOE_ERR_ARG
 
 
+def test_sparse_clip_rejections():
+    lib = moe.load()
+    ok = ctypes.c_void_p(0x100000)
+    cfg = _cfg()
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.moe_sparse_clip(ctypes.byref(cfg), None, None, ok, ok, bad, ok, ok, None) == \
+            _lib.MOE_ERR_ARG
+        assert "max_norm" in lib.moe_last_error().decode()
+    assert lib.moe_sparse_clip(ctypes.byref(cfg), None, None, ok, None, 1.0, ok, ok, None) == _lib.MOE_ERR_ARG
+    assert lib.moe_last_error().decode().startswith("dw2")
+    assert lib.moe_sparse_clip(ctypes.byref(cfg), None, None, ok, ok, 1.0, None, ok, None) == _lib.MOE_ERR_ARG
+    assert lib.moe_last_error().decode().startswith("norm_coef")
+
+
 def test_binding_raises_on_error():
     cfg = moe.make_config(10, 64, 64, 4, 5, 1.0)
     with pytest.raises(moe.MoeError, match="k must be"):

@@ -151,6 +151,34 @@ def test_backward_matches_oracle(name):
             assert torch.equal(val, again[key]), f"{key} differs between calls"
 
 
+@pytest.mark.parametrize("name", ["zipf_small_bf16", "rre_small_bf16", "tiny_switch_f32"])
+def test_sparse_clip(name):
+    """moe_sparse_clip on the gradients moe_backward wrote: norm and coefficient against the
+    oracle's SparseClip of the same gradient values, clipped values equal to each gradient
+    times the float32 coefficient rounded to its dtype."""
+    wl = W.TEST_WORKLOADS[name]
+    print(f"[gpu] sparse clip {name}", flush=True)
+    inputs = W.make_inputs(wl)
+    dev = Dev(wl, inputs)
+    got = dev.run_backward(make_dy(wl))
+    host = {k: (None if v is None else to_host_f64(v)) for k, v in got.items() if k != "dx"}
+    _, norm, _ = oracle.sparse_clip(host, wl.E, 1.0)
+    max_norm = norm / 4            # clipping active
+    _, norm, coef = oracle.sparse_clip(host, wl.E, max_norm)
+    nc = torch.empty(2, dtype=torch.float32, device="cuda")
+    bws = moe.alloc_backward_workspace(dev.cfg)
+    before = {k: (None if v is None else v.clone()) for k, v in got.items()}
+    moe.sparse_clip(dev.cfg, got["dw_r"], got["dbias"], got["dw1"], got["dw2"], max_norm, nc, bws)
+    torch.cuda.synchronize()
+    n_gpu, c_gpu = (float(v) for v in nc.cpu())
+    assert abs(n_gpu - norm) <= 2 ** -22 * norm and abs(c_gpu - coef) <= 2 ** -22 * coef
+    for key in ("dw_r", "dbias", "dw1", "dw2"):
+        if got[key] is None:
+            continue
+        want = (before[key].float() * torch.tensor(c_gpu, dtype=torch.float32, device="cuda")).to(got[key].dtype)
+        assert torch.equal(got[key], want), key
+
+
 @pytest.mark.parametrize("name", ["switch_small_bf16", "xmoe_small_bf16", "tiny_switch_f32"])
 def test_combine_alone(name):
     """Combine on oracle-provided expert outputs (rounded to the storage dtype)."""

@@ -175,6 +175,15 @@ def _backward_variant(mode):
     return bwd
 
 
+def _sparse_clip_kappa_not_squared(grads, E, max_norm):
+    dense = [g for g in (grads.get("dw_r"), grads.get("dbias")) if g is not None]
+    sq_d = sum(float(np.sum(np.asarray(g, np.float64) ** 2)) for g in dense)
+    sq_m = sum(float(np.sum(np.asarray(g, np.float64) ** 2)) for g in (grads["dw1"], grads["dw2"]))
+    norm = math.sqrt(sq_d + sq_m / math.sqrt(E))
+    coef = min(1.0, max_norm / (norm + 1e-6))
+    return {k: (None if v is None else np.asarray(v, np.float64) * coef) for k, v in grads.items()}, norm, coef
+
+
 ALL_PINS = [
     lambda rng: P.check_worked_fixture("switch_top1_worked.json"),
     lambda rng: P.check_worked_fixture("top2_priority_worked.json"),
@@ -185,7 +194,7 @@ ALL_PINS = [
     lambda rng: P.check_gelu_values(), P.check_dense_equals_sparse, P.check_single_expert_is_mlp,
     P.check_k_equals_E_is_softmax_mixture, P.check_expert_permutation, P.check_aux_loss,
     P.check_backward_autograd, P.check_backward_finite_differences,
-    P.check_backward_single_expert_is_mlp, P.check_backward_rre_no_router_grad,
+    P.check_backward_single_expert_is_mlp, P.check_backward_rre_no_router_grad, P.check_sparse_clip,
 ]
 
 MUTATIONS = {
@@ -210,6 +219,7 @@ MUTATIONS = {
     "backward_softmax_jacobian_sign": ("backward", _backward_variant("jacobian_sign")),
     "backward_softmax_jacobian_diagonal": ("backward", _backward_variant("jacobian_diag_only")),
     "backward_dw1_wrong": ("backward", _backward_variant("dw1_from_hidden")),
+    "sparse_clip_kappa_not_squared": ("sparse_clip", _sparse_clip_kappa_not_squared),
 }
 
 

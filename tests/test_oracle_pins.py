@@ -102,3 +102,7 @@ def test_backward_single_expert_is_mlp(rng):
 
 def test_backward_rre(rng):
     P.check_backward_rre_no_router_grad(rng)
+
+
+def test_sparse_clip(rng):
+    P.check_sparse_clip(rng)
