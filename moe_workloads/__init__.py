@@ -12,6 +12,8 @@ Array conventions (NumPy, host memory):
   * ``bias``     [E] f32 or None     per-expert router logit bias (Zipf skew)
   * ``group_id`` [T] int32 or None   expert group of each token (RRE only)
   * ``w1[e]``    [d_ff, d_model]     expert up-projection, stored out x in
+                 ([2 d_ff, d_model] for the GLU FFN: the activated projection's
+                 rows, then the linear gate projection's rows)
   * ``w2[e]``    [d_model, d_ff]     expert down-projection, stored out x in
 
 Value distributions follow the workload descriptions of the Switch/X-MoE/
@@ -35,7 +37,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "TEST_WORKLOADS", "get", "make_inputs",
-    "expert_weights", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "expert_weights", "w1_rows", "f32_to_bf16_bits", "bf16_bits_to_f32",
 ]
 
 
@@ -57,6 +59,7 @@ class Workload:
     rre_seed: int = 0
     # "dyadic" (integers/8) or "gauss" (N(0, 1/d_model) rounded to fp32) router weight
     w_r_dist: str = "dyadic"
+    glu: bool = False        # gated-linear-unit expert FFN (w1 holds 2 * d_ff rows)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -103,6 +106,20 @@ TEST_WORKLOADS = {
                                capacity_factor=1.0, act="gelu", dtype="bf16"),
     "wide_top2_bf16": Workload("wide_top2_bf16", T=1200, d_model=384, d_ff=256, E=40, k=2,
                                capacity_factor=1.0, act="relu", dtype="bf16"),
+    # gated-linear-unit experts, one per grouped-GEMM capacity range: C = 63 (384-row
+    # weight tiles), 100, 150, 230 (LDS-tiled), 500 (256 x 256 tiles), and float32
+    "geglu_wide_top1_bf16": Workload("geglu_wide_top1_bf16", T=1500, d_model=768, d_ff=384, E=24,
+                                     k=1, capacity_factor=1.0, act="gelu", dtype="bf16", glu=True),
+    "reglu_c100_bf16": Workload("reglu_c100_bf16", T=1000, d_model=256, d_ff=320, E=10, k=1,
+                                capacity_factor=1.0, act="relu", dtype="bf16", glu=True),
+    "geglu_c150_bf16": Workload("geglu_c150_bf16", T=1500, d_model=256, d_ff=192, E=10, k=1,
+                                capacity_factor=1.0, act="gelu", dtype="bf16", glu=True),
+    "geglu_top2_bf16": Workload("geglu_top2_bf16", T=1100, d_model=320, d_ff=448, E=12, k=2,
+                                capacity_factor=1.25, act="gelu", dtype="bf16", glu=True),
+    "reglu_c500_bf16": Workload("reglu_c500_bf16", T=3000, d_model=256, d_ff=256, E=6, k=1,
+                                capacity_factor=1.0, act="relu", dtype="bf16", glu=True),
+    "reglu_small_f32": Workload("reglu_small_f32", T=600, d_model=128, d_ff=192, E=8, k=1,
+                                capacity_factor=1.25, act="relu", dtype="f32", glu=True),
 }
 
 
@@ -149,14 +166,19 @@ def _store(a32: np.ndarray, dtype: str) -> np.ndarray:
     return f32_to_bf16_bits(a32) if dtype == "bf16" else np.ascontiguousarray(a32, np.float32)
 
 
+def w1_rows(wl: Workload) -> int:
+    """Rows of one expert's w1: d_ff, or 2 * d_ff for the GLU FFN."""
+    return 2 * wl.d_ff if wl.glu else wl.d_ff
+
+
 def expert_weights(wl: Workload, e: int):
-    """(w1[e] [d_ff, d_model], w2[e] [d_model, d_ff]) in the workload dtype."""
+    """(w1[e] [w1_rows, d_model], w2[e] [d_model, d_ff]) in the workload dtype."""
     kids = _children(wl)
     s1 = kids["w1"].spawn(wl.E)[e]
     s2 = kids["w2"].spawn(wl.E)[e]
     r1 = np.random.Generator(np.random.PCG64(s1))
     r2 = np.random.Generator(np.random.PCG64(s2))
-    w1 = r1.standard_normal((wl.d_ff, wl.d_model), dtype=np.float32)
+    w1 = r1.standard_normal((w1_rows(wl), wl.d_model), dtype=np.float32)
     w1 *= np.float32(1.0 / math.sqrt(wl.d_model))
     w2 = r2.standard_normal((wl.d_model, wl.d_ff), dtype=np.float32)
     w2 *= np.float32(1.0 / math.sqrt(wl.d_ff))
@@ -177,9 +199,9 @@ def for_each_expert(wl: Workload, fn: Callable[[int, np.ndarray, np.ndarray], No
 
 
 def stacked_weights(wl: Workload):
-    """All experts stacked: w1 [E, d_ff, d_model], w2 [E, d_model, d_ff] (host memory)."""
+    """All experts stacked: w1 [E, w1_rows, d_model], w2 [E, d_model, d_ff] (host memory)."""
     dt = np.uint16 if wl.dtype == "bf16" else np.float32
-    w1 = np.empty((wl.E, wl.d_ff, wl.d_model), dt)
+    w1 = np.empty((wl.E, w1_rows(wl), wl.d_model), dt)
     w2 = np.empty((wl.E, wl.d_model, wl.d_ff), dt)
 
     def put(e, a, b):

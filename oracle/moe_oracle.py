@@ -18,6 +18,9 @@ passage of the source pages it follows:
   [PanGu]    "PanGu-Sigma: Towards Trillion Parameter Language Model with Sparse
              Heterogeneous Computing" (nubint.ai review), proposed method:
              Random Routed Experts (RRE).
+  [Mosaic]   "MosaicBERT: A Bidirectional Encoder Optimized for Fast
+             Pretraining" (nubint.ai review), methodology: gated linear units
+             in the feed-forward layer (the GLU expert variant).
 
 Where the pages leave a step open, the reading taken is stated at the function.
 
@@ -240,16 +243,32 @@ def act_fn(z: np.ndarray, act: str) -> np.ndarray:
     raise ValueError(act)
 
 
-def expert_apply(xrows: np.ndarray, w1_e: np.ndarray, w2_e: np.ndarray, act: str) -> np.ndarray:
-    """One expert E_i on a batch of rows: act(x W1) W2 with W1 = w1_e^T, W2 = w2_e^T (float64).
+def expert_hidden(xrows: np.ndarray, w1_e: np.ndarray, act: str, glu: bool = False) -> np.ndarray:
+    """Hidden activations H of one expert on a batch of rows (float64).
 
-    w1_e is stored [d_ff, d_model] and w2_e [d_model, d_ff] (output x input).
+    Plain FFN ([Switch] 2.1): H = act(x W1), W1 = w1_e^T, w1_e stored [d_ff, d_model].
+    GLU FFN ([Mosaic] methodology, gated linear units in the feed-forward layer):
+    H = act(x W) * (x V), the product elementwise.  Reading taken where the page is
+    silent: the activation is the layer's (ReLU or exact GELU), it is applied to the
+    x W branch only, and the two projections are stored stacked in one matrix
+    w1_e [2 d_ff, d_model], rows 0 .. d_ff - 1 being W^T and rows d_ff .. 2 d_ff - 1
+    being V^T, so both come from one product x w1_e^T.
     """
-    hdn = act_fn(xrows @ as_f64(w1_e).T, act)
-    return hdn @ as_f64(w2_e).T
+    z = xrows @ as_f64(w1_e).T
+    if not glu:
+        return act_fn(z, act)
+    f = z.shape[1] // 2
+    return act_fn(z[:, :f], act) * z[:, f:]
 
 
-def expert_ffn(x_e: list, weights: Callable[[int], tuple], act: str) -> list:
+def expert_apply(xrows: np.ndarray, w1_e: np.ndarray, w2_e: np.ndarray, act: str,
+                 glu: bool = False) -> np.ndarray:
+    """One expert E_i on a batch of rows: H W2 with H from ``expert_hidden`` and
+    W2 = w2_e^T, w2_e stored [d_model, d_ff] (output x input).  float64."""
+    return expert_hidden(xrows, w1_e, act, glu) @ as_f64(w2_e).T
+
+
+def expert_ffn(x_e: list, weights: Callable[[int], tuple], act: str, glu: bool = False) -> list:
     """Apply every expert to its batch; ``weights(e)`` returns (w1_e, w2_e)."""
     out = []
     for e, rows in enumerate(x_e):
@@ -257,8 +276,13 @@ def expert_ffn(x_e: list, weights: Callable[[int], tuple], act: str) -> list:
             out.append(np.zeros((0, rows.shape[1] if rows.ndim == 2 else 0)))
             continue
         w1_e, w2_e = weights(e)
-        out.append(expert_apply(rows, w1_e, w2_e, act))
+        out.append(expert_apply(rows, w1_e, w2_e, act, glu))
     return out
+
+
+def is_glu(wl) -> bool:
+    """Whether a workload record uses the GLU expert FFN (records without the field do not)."""
+    return bool(getattr(wl, "glu", False))
 
 
 # ---------------------------------------------------------------------------
@@ -301,7 +325,8 @@ def forward(wl, inputs, weights: Optional[Callable[[int], tuple]] = None) -> dic
     """The full layer: router -> dispatch -> gather -> expert FFN -> combine.
 
     ``inputs`` holds x, w_r, bias, group_id and (unless ``weights`` is given) the
-    stacked expert weights w1 [E, d_ff, d_model], w2 [E, d_model, d_ff].
+    stacked expert weights w1 [E, d_ff, d_model] ([E, 2 d_ff, d_model] for the GLU
+    FFN, see ``expert_hidden``), w2 [E, d_model, d_ff].
     Returns every intermediate: expert_idx, gate, logits, slot, expert_count,
     slot_token, x_e (list), y_e (list) and y [T, d_model] (float64).
     """
@@ -312,7 +337,7 @@ def forward(wl, inputs, weights: Optional[Callable[[int], tuple]] = None) -> dic
     idx, gate, logits = route(wl, inputs)
     slot, count, slot_token = dispatch(idx, wl.E, C)
     x_e = gather(inputs["x"], slot_token, count)
-    y_e = expert_ffn(x_e, weights, wl.act)
+    y_e = expert_ffn(x_e, weights, wl.act, is_glu(wl))
     y = combine(y_e, idx, slot, gate, wl.d_model)
     return dict(capacity=C, expert_idx=idx, gate=gate, logits=logits, slot=slot,
                 expert_count=count, slot_token=slot_token, x_e=x_e, y_e=y_e, y=y)
@@ -340,7 +365,7 @@ def forward_rows(wl, inputs, rows: np.ndarray, weights: Callable[[int], tuple],
             if e not in cache:
                 cache[e] = weights(e)
             w1_e, w2_e = cache[e]
-            ye = expert_apply(as_f64(xf[t:t + 1]), w1_e, w2_e, wl.act)[0]
+            ye = expert_apply(as_f64(xf[t:t + 1]), w1_e, w2_e, wl.act, is_glu(wl))[0]
             out[i] += float(routing["gate"][t, c]) * ye
     return out
 
@@ -414,12 +439,14 @@ def backward(wl, inputs, fwd: dict, dy: np.ndarray,
       expert term: dE = p_e dy[t]; with Z = x W1_e, H = act(Z), E = H W2_e:
         dW2_e += dE^T H, dH = dE W2_e^T, dZ = dH * act'(Z),
         dW1_e += dZ^T x, dx[t] += dZ W1_e^T;
+      GLU FFN (``expert_hidden``): Z = (Za, Zb) = (x W, x V), H = act(Za) * Zb, so
+        dZ = (dH * Zb * act'(Za), dH * act(Za)) over the stacked w1 rows;
       gate term: dp_e(t) = dy[t] . E_e(x_t), and through the softmax Jacobian
         dh = p * (dp - <p, dp>), then dx[t] += dh W_r, dW_r += dh^T x, dbias += dh.
     Random routed experts have constant gates 1: no router gradient (dw_r, dbias None).
     Weights are taken at their stored values (``weights(e)`` -> (w1_e, w2_e) in the
     stored [d_ff, d_model] / [d_model, d_ff] layout), every product in float64.
-    Returns dx [T, d], dw1 [E, f, d], dw2 [E, d, f], dw_r [E, d] or None,
+    Returns dx [T, d], dw1 [E, f, d] ([E, 2f, d] for GLU), dw2 [E, d, f], dw_r [E, d] or None,
     dbias [E] or None, dgate [T, k] (dL/dp of each served choice, 0 if dropped).
     """
     if weights is None:
@@ -429,7 +456,8 @@ def backward(wl, inputs, fwd: dict, dy: np.ndarray,
     T, d, f, E, k = wl.T, wl.d_model, wl.d_ff, wl.E, wl.k
     x = as_f64(inputs["x"])
     dx = np.zeros((T, d))
-    dw1 = np.zeros((E, f, d))
+    glu = is_glu(wl)
+    dw1 = np.zeros((E, 2 * f if glu else f, d))
     dw2 = np.zeros((E, d, f))
     dgate = np.zeros((T, k))
     topk_route = wl.route == "topk"
@@ -442,14 +470,22 @@ def backward(wl, inputs, fwd: dict, dy: np.ndarray,
         owners = [served_choice(fwd, e, s) for s in range(n)]
         xe = x[[t for t, _ in owners]]
         z = xe @ w1_e.T
-        hdn = act_fn(z, wl.act)
+        if glu:
+            za, zb = z[:, :f], z[:, f:]
+            hdn = act_fn(za, wl.act) * zb
+        else:
+            hdn = act_fn(z, wl.act)
         ye = hdn @ w2_e.T
         g = np.array([p[t, e] if topk_route else 1.0 for t, _ in owners])
         dye = g[:, None] * dy[[t for t, _ in owners]]
         for s, (t, c) in enumerate(owners):
             dgate[t, c] = float(dy[t] @ ye[s])
         dw2[e] = dye.T @ hdn
-        dz = (dye @ w2_e) * act_grad(z, wl.act)
+        dhdn = dye @ w2_e
+        if glu:
+            dz = np.concatenate([dhdn * zb * act_grad(za, wl.act), dhdn * act_fn(za, wl.act)], axis=1)
+        else:
+            dz = dhdn * act_grad(z, wl.act)
         dw1[e] = dz.T @ xe
         dxe = dz @ w1_e
         for s, (t, _) in enumerate(owners):

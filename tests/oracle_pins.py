@@ -285,8 +285,8 @@ def check_gelu_values():
     np.testing.assert_array_equal(O.act_fn(np.array([-2.0, 0.0, 3.5]), "relu"), [0.0, 0.0, 3.5])
 
 
-def _rand_layer(rng, T, d, f, E, k, cf, act, zipf=False, ties=False):
-    wl = _WL(T=T, d_model=d, d_ff=f, E=E, k=k, capacity_factor=cf, act=act)
+def _rand_layer(rng, T, d, f, E, k, cf, act, zipf=False, ties=False, glu=False):
+    wl = _WL(T=T, d_model=d, d_ff=f, E=E, k=k, capacity_factor=cf, act=act, glu=glu)
     x = (rng.integers(-8, 9, size=(T, d)) / 8).astype(np.float32)
     w_r = (rng.integers(-8, 9, size=(E, d)) / 8).astype(np.float32)
     if not ties:
@@ -296,7 +296,7 @@ def _rand_layer(rng, T, d, f, E, k, cf, act, zipf=False, ties=False):
         bias = None
     if zipf:
         bias = (-1.1 * np.log(np.arange(1, E + 1))).astype(np.float32)
-    w1 = (rng.normal(size=(E, f, d)) / math.sqrt(d)).astype(np.float32)
+    w1 = (rng.normal(size=(E, 2 * f if glu else f, d)) / math.sqrt(d)).astype(np.float32)
     w2 = (rng.normal(size=(E, d, f)) / math.sqrt(f)).astype(np.float32)
     return wl, {"x": x, "w_r": w_r, "bias": bias, "group_id": None, "w1": w1, "w2": w2}
 
@@ -320,7 +320,12 @@ def dense_layer(wl, inputs, r):
     xe = np.einsum("tec,td->ecd", D, x)
     w1 = O.as_f64(inputs["w1"])
     w2 = O.as_f64(inputs["w2"])
-    hid = O.act_fn(np.einsum("ecd,efd->ecf", xe, w1), wl.act)
+    zz = np.einsum("ecd,efd->ecf", xe, w1)
+    if getattr(wl, "glu", False):
+        f = wl.d_ff
+        hid = O.act_fn(zz[:, :, :f], wl.act) * zz[:, :, f:]
+    else:
+        hid = O.act_fn(zz, wl.act)
     ye = np.einsum("ecf,edf->ecd", hid, w2)
     return np.einsum("tec,ecd->td", Wc, ye)
 
@@ -330,9 +335,47 @@ def check_dense_equals_sparse(rng):
                                            (90, 8, 12, 6, 2, 1.0, "gelu", False),
                                            (50, 16, 8, 5, 2, 0.5, "gelu", True),
                                            (33, 8, 8, 3, 3, 1.0, "relu", False)]:
-        wl, inp = _rand_layer(rng, T, d, f, E, k, cf, act, zipf)
-        r = O.forward(wl, inp)
-        np.testing.assert_allclose(r["y"], dense_layer(wl, inp, r), rtol=1e-12, atol=1e-12)
+        for glu in (False, True):
+            wl, inp = _rand_layer(rng, T, d, f, E, k, cf, act, zipf, glu=glu)
+            r = O.forward(wl, inp)
+            np.testing.assert_allclose(r["y"], dense_layer(wl, inp, r), rtol=1e-12, atol=1e-12)
+
+
+def check_glu_coordinate_gate(rng):
+    """GLU FFN (MosaicBERT review, methodology) reduced to the plain FFN: with every V
+    row a multiple a_j of the unit vector of input coordinate i, unit j's gate is
+    a_j x_i, so the GLU expert equals x_i times the plain expert whose w2 columns are
+    scaled by a.  Pins which branch takes the activation, the order of the stacked
+    halves and the pairing of W row j with V row j."""
+    T, d, f = 20, 12, 10
+    x = (rng.integers(-8, 9, size=(T, d)) / 8).astype(np.float64)
+    for act in ("relu", "gelu"):
+        W = rng.normal(size=(f, d)) / math.sqrt(d)
+        w2 = rng.normal(size=(d, f)) / math.sqrt(f)
+        a = rng.normal(size=f)
+        i = int(rng.integers(0, d))
+        V = np.zeros((f, d))
+        V[:, i] = a
+        got = O.expert_apply(x, np.concatenate([W, V]), w2, act, glu=True)
+        ref = x[:, i:i + 1] * O.expert_apply(x, W, w2 * a[None, :], act)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def check_glu_linear_in_v(rng):
+    """The GLU expert is linear in V (x V enters the product once, unactivated):
+    y(V1 + V2) = y(V1) + y(V2) and y(c V) = c y(V); with the coordinate-gate pin this
+    ties the GLU expert to the plain one for every V."""
+    T, d, f = 16, 8, 12
+    x = (rng.integers(-8, 9, size=(T, d)) / 8).astype(np.float64)
+    for act in ("relu", "gelu"):
+        W, V1, V2 = (rng.normal(size=(f, d)) for _ in range(3))
+        w2 = rng.normal(size=(d, f))
+
+        def y(V):
+            return O.expert_apply(x, np.concatenate([W, V]), w2, act, glu=True)
+
+        np.testing.assert_allclose(y(V1 + V2), y(V1) + y(V2), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(y(-2.5 * V1), -2.5 * y(V1), rtol=1e-12, atol=1e-12)
 
 
 def check_single_expert_is_mlp(rng):
@@ -443,8 +486,12 @@ def _torch_dense_grads(wl, inp, r, dy):
     act = torch.relu if wl.act == "relu" else (lambda z: torch.nn.functional.gelu(z, approximate="none"))
     y = torch.zeros(T, wl.d_model, dtype=torch.float64)
     mt = torch.tensor(m)
+    f = wl.d_ff
     for e in range(E):
-        fe = act(x @ w1[e].T) @ w2[e].T
+        if getattr(wl, "glu", False):
+            fe = (act(x @ w1[e][:f].T) * (x @ w1[e][f:].T)) @ w2[e].T
+        else:
+            fe = act(x @ w1[e].T) @ w2[e].T
         y = y + (mt[:, e] * p[:, e])[:, None] * fe
     (y * torch.tensor(dy)).sum().backward()
     out = dict(dx=x.grad.numpy(), dw_r=w_r.grad.numpy(), dw1=w1.grad.numpy(), dw2=w2.grad.numpy())
@@ -455,11 +502,13 @@ def _torch_dense_grads(wl, inp, r, dy):
 def check_backward_autograd(rng):
     # dyadic x and w_r: the float32 logits the oracle routes on equal the float64 ones;
     # the tiny bias only breaks ties (rounded to float32 once, like the oracle's)
-    for (T, d, f, E, k, cf, act, zipf) in [(40, 16, 24, 4, 1, 1.0, "gelu", False),
-                                           (60, 8, 12, 6, 2, 1.0, "gelu", False),
-                                           (50, 16, 8, 5, 2, 0.5, "relu", True),
-                                           (24, 8, 8, 3, 3, 2.0, "gelu", False)]:
-        wl, inp = _rand_layer(rng, T, d, f, E, k, cf, act, zipf)
+    for (T, d, f, E, k, cf, act, zipf, glu) in [(40, 16, 24, 4, 1, 1.0, "gelu", False, False),
+                                                (60, 8, 12, 6, 2, 1.0, "gelu", False, False),
+                                                (50, 16, 8, 5, 2, 0.5, "relu", True, False),
+                                                (24, 8, 8, 3, 3, 2.0, "gelu", False, False),
+                                                (40, 16, 12, 4, 2, 1.0, "gelu", False, True),
+                                                (36, 8, 8, 3, 1, 1.0, "relu", True, True)]:
+        wl, inp = _rand_layer(rng, T, d, f, E, k, cf, act, zipf, glu=glu)
         if not zipf:
             inp["bias"] = None
             inp["x"] = inp["x"] + (rng.integers(0, 64, size=inp["x"].shape) / 512).astype(np.float32)
@@ -480,27 +529,31 @@ def check_backward_finite_differences(rng):
     # central differences of L = <y, dy> in the expert weights (GELU: smooth; the
     # routing does not depend on w1, w2).  The router weight is pinned by autograd
     # instead: the forward stores float32 gates, whose rounding swamps a small step.
+    # GLU: both halves of the stacked w1 (the activated W rows and the linear V rows)
     T, d, f, E, k = 30, 8, 10, 3, 2
-    wl, inp = _rand_layer(rng, T, d, f, E, k, 1.0, "gelu")
-    inp["bias"] = None
-    for key in ("w1", "w2"):
-        inp[key] = inp[key].astype(np.float64)
-    r = O.forward(wl, inp)
-    dy = rng.normal(size=(T, d))
-    g = O.backward(wl, inp, r, dy)
+    for glu in (False, True):
+        wl, inp = _rand_layer(rng, T, d, f, E, k, 1.0, "gelu", glu=glu)
+        inp["bias"] = None
+        for key in ("w1", "w2"):
+            inp[key] = inp[key].astype(np.float64)
+        r = O.forward(wl, inp)
+        dy = rng.normal(size=(T, d))
+        g = O.backward(wl, inp, r, dy)
 
-    def loss(i2):
-        return float((O.forward(wl, i2)["y"] * dy).sum())
+        def loss(i2):
+            return float((O.forward(wl, i2)["y"] * dy).sum())
 
-    for key, grad in (("w1", g["dw1"]), ("w2", g["dw2"])):
-        for _ in range(6):
-            idx = tuple(int(rng.integers(0, n)) for n in inp[key].shape)
-            eps = 1e-5
-            ip, im = dict(inp), dict(inp)
-            ip[key] = inp[key].copy(); ip[key][idx] += eps
-            im[key] = inp[key].copy(); im[key][idx] -= eps
-            fd = (loss(ip) - loss(im)) / (2 * eps)
-            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (key, idx, fd, grad[idx])
+        for key, grad in (("w1", g["dw1"]), ("w2", g["dw2"])):
+            picks = [tuple(int(rng.integers(0, n)) for n in inp[key].shape) for _ in range(6)]
+            if glu and key == "w1":  # at least three entries in each half
+                picks = [(e, (j % f) + (f if q >= 3 else 0), c) for q, (e, j, c) in enumerate(picks)]
+            for idx in picks:
+                eps = 1e-5
+                ip, im = dict(inp), dict(inp)
+                ip[key] = inp[key].copy(); ip[key][idx] += eps
+                im[key] = inp[key].copy(); im[key][idx] -= eps
+                fd = (loss(ip) - loss(im)) / (2 * eps)
+                assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (glu, key, idx, fd, grad[idx])
 
 
 def check_backward_single_expert_is_mlp(rng):

@@ -92,10 +92,81 @@ def _act_tanh_gelu(z, act):
     return _orig["act_fn"](z, act)
 
 
-def _expert_apply_w2_untransposed(xrows, w1_e, w2_e, act):
-    hdn = O.act_fn(xrows @ O.as_f64(w1_e).T, act)
+def _expert_apply_w2_untransposed(xrows, w1_e, w2_e, act, glu=False):
+    hdn = O.expert_hidden(xrows, w1_e, act, glu)
     w2 = O.as_f64(w2_e)
     return hdn @ w2.reshape(w2.shape[1], w2.shape[0])
+
+
+def _glu_hidden_variant(mode):
+    def hidden(xrows, w1_e, act, glu=False):
+        if not glu:
+            return _orig["expert_hidden"](xrows, w1_e, act, glu)
+        z = xrows @ O.as_f64(w1_e).T
+        f = z.shape[1] // 2
+        za, zb = z[:, :f], z[:, f:]
+        if mode == "act_on_linear_branch":
+            return za * O.act_fn(zb, act)
+        if mode == "act_on_product":
+            return O.act_fn(za * zb, act)
+        if mode == "mispaired":
+            return O.act_fn(za, act) * zb[:, ::-1]
+        raise ValueError(mode)
+    return hidden
+
+
+def _backward_glu_variant(mode):
+    """The oracle backward, with a planted mistake in the GLU part of dZ (test code only)."""
+    def bwd(wl, inputs, fwd, dy, weights=None):
+        if not getattr(wl, "glu", False):
+            return _orig["backward"](wl, inputs, fwd, dy, weights)
+        w1, w2 = inputs["w1"], inputs["w2"]
+        dy = np.asarray(dy, np.float64)
+        T, d, f, E, k = wl.T, wl.d_model, wl.d_ff, wl.E, wl.k
+        x = O.as_f64(inputs["x"])
+        dx, dw1, dw2, dgate = np.zeros((T, d)), np.zeros((E, 2 * f, d)), np.zeros((E, d, f)), np.zeros((T, k))
+        topk_route = wl.route == "topk"
+        p = O.softmax(fwd["logits"]) if topk_route else None
+        for e in range(E):
+            n = int(fwd["expert_count"][e])
+            if n == 0:
+                continue
+            w1_e, w2_e = O.as_f64(w1[e]), O.as_f64(w2[e])
+            owners = [O.served_choice(fwd, e, s) for s in range(n)]
+            xe = x[[t for t, _ in owners]]
+            z = xe @ w1_e.T
+            za, zb = z[:, :f], z[:, f:]
+            hdn = O.act_fn(za, wl.act) * zb
+            ye = hdn @ w2_e.T
+            g = np.array([p[t, e] if topk_route else 1.0 for t, _ in owners])
+            dye = g[:, None] * dy[[t for t, _ in owners]]
+            for s, (t, c) in enumerate(owners):
+                dgate[t, c] = float(dy[t] @ ye[s])
+            dw2[e] = dye.T @ hdn
+            dh = dye @ w2_e
+            if mode == "gate_half_uses_act_grad":
+                dz = np.concatenate([dh * zb * O.act_grad(za, wl.act), dh * O.act_grad(za, wl.act)], axis=1)
+            elif mode == "act_half_without_gate":
+                dz = np.concatenate([dh * O.act_grad(za, wl.act), dh * O.act_fn(za, wl.act)], axis=1)
+            else:
+                raise ValueError(mode)
+            dw1[e] = dz.T @ xe
+            dxe = dz @ w1_e
+            for s, (t, _) in enumerate(owners):
+                dx[t] += dxe[s]
+        dw_r = dbias = None
+        if topk_route:
+            dp = np.zeros((T, E))
+            for t in range(T):
+                for c in range(k):
+                    if int(fwd["slot"][t, c]) >= 0:
+                        dp[t, int(fwd["expert_idx"][t, c])] += dgate[t, c]
+            dh_r = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dx += dh_r @ O.as_f64(inputs["w_r"])
+            dw_r = dh_r.T @ x
+            dbias = dh_r.sum(axis=0) if inputs.get("bias") is not None else None
+        return dict(dx=dx, dw1=dw1, dw2=dw2, dw_r=dw_r, dbias=dbias, dgate=dgate)
+    return bwd
 
 
 def _splitmix_bad_shift(seed, n):
@@ -192,6 +263,7 @@ ALL_PINS = [
     P.check_topk_rank, P.check_gate_raw, lambda rng: P.check_splitmix_reference(), P.check_rre,
     P.check_dispatch_invariants, P.check_dispatch_no_drop, P.check_choice_priority,
     lambda rng: P.check_gelu_values(), P.check_dense_equals_sparse, P.check_single_expert_is_mlp,
+    P.check_glu_coordinate_gate, P.check_glu_linear_in_v,
     P.check_k_equals_E_is_softmax_mixture, P.check_expert_permutation, P.check_aux_loss,
     P.check_backward_autograd, P.check_backward_finite_differences,
     P.check_backward_single_expert_is_mlp, P.check_backward_rre_no_router_grad, P.check_sparse_clip,
@@ -212,6 +284,11 @@ MUTATIONS = {
     "combine_wrong_choice_gate": ("combine", _combine_first_gate),
     "gelu_tanh_approximation": ("act_fn", _act_tanh_gelu),
     "w2_not_transposed": ("expert_apply", _expert_apply_w2_untransposed),
+    "glu_act_on_linear_branch": ("expert_hidden", _glu_hidden_variant("act_on_linear_branch")),
+    "glu_act_on_product": ("expert_hidden", _glu_hidden_variant("act_on_product")),
+    "glu_units_mispaired": ("expert_hidden", _glu_hidden_variant("mispaired")),
+    "backward_glu_gate_half_uses_act_grad": ("backward", _backward_glu_variant("gate_half_uses_act_grad")),
+    "backward_glu_act_half_without_gate": ("backward", _backward_glu_variant("act_half_without_gate")),
     "splitmix_wrong_shift": ("splitmix64", _splitmix_bad_shift),
     "rre_off_by_one_token": ("route_rre", _rre_shifted),
     "gelu_grad_without_density_term": ("act_grad", _gelu_grad_no_density),

@@ -72,6 +72,14 @@ def test_dense_equals_sparse(rng):
     P.check_dense_equals_sparse(rng)
 
 
+def test_glu_coordinate_gate(rng):
+    P.check_glu_coordinate_gate(rng)
+
+
+def test_glu_linear_in_v(rng):
+    P.check_glu_linear_in_v(rng)
+
+
 def test_single_expert_is_mlp(rng):
     P.check_single_expert_is_mlp(rng)
 

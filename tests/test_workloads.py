@@ -32,7 +32,7 @@ def test_small_inputs_deterministic_and_on_grid():
             assert set(np.unique(a["w_r"] * 8).tolist()) <= set(range(-8, 9))
         else:
             assert a["group_id"].min() >= 0 and a["group_id"].max() < wl.n_groups
-        assert a["w1"].shape == (wl.E, wl.d_ff, wl.d_model)
+        assert a["w1"].shape == (wl.E, W.w1_rows(wl), wl.d_model)
         assert a["w2"].shape == (wl.E, wl.d_model, wl.d_ff)
         # one expert regenerated alone equals its slice of the stack
         w1e, w2e = W.expert_weights(wl, wl.E - 1)
