@@ -48,7 +48,12 @@ extern "C" {
 #endif
 
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
-typedef enum { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1 } moe_act;
+/* Expert activation.  RELU / GELU: the plain FFN act(x W1) W2 (GELU with the
+ * exact erf).  REGLU / GEGLU: the gated-linear-unit FFN of the MosaicBERT review
+ * (methodology: gated linear units in the feed-forward layer),
+ * (act(x W) * (x V)) W2 with act ReLU / GELU, the product elementwise; W and V
+ * are stored stacked in w1 (see moe_expert_ffn), so w1 has 2 * d_ff rows. */
+typedef enum { MOE_ACT_RELU = 0, MOE_ACT_GELU = 1, MOE_ACT_REGLU = 2, MOE_ACT_GEGLU = 3 } moe_act;
 typedef enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_RRE = 1 } moe_route;
 
 enum {
@@ -68,7 +73,7 @@ typedef struct moe_config {
   int32_t route;           /* moe_route                                              */
   int32_t n_groups;        /* RRE: expert groups (experts g*E/n_groups ... next)     */
   uint64_t rre_seed;       /* RRE: SplitMix64 seed                                   */
-  int32_t act;             /* moe_act: ReLU, or GELU with the exact erf              */
+  int32_t act;             /* moe_act: ReLU, GELU (exact erf), or their GLU forms   */
   int32_t dtype;           /* moe_dtype of x, w1, w2, x_e, y_e, y                    */
 } moe_config;
 
@@ -93,7 +98,7 @@ typedef enum {
   MOE_WS_EXPERT_COUNT = 3, /* int32 [E]                                      */
   MOE_WS_SLOT_TOKEN = 4,   /* int32 [E, C]                                   */
   MOE_WS_X_E = 5,          /* dtype [E, C, d_model]                          */
-  MOE_WS_HIDDEN = 6,       /* dtype [E, C, d_ff]  act(x_e W1) per expert     */
+  MOE_WS_HIDDEN = 6,       /* dtype [E, C, d_ff]  hidden activations H       */
   MOE_WS_Y_E = 7,          /* dtype [E, C, d_model]                          */
   MOE_WS_N_REGIONS = 8
 } moe_ws_region;
@@ -156,22 +161,26 @@ int moe_dispatch(const moe_config* cfg, const void* x, const int32_t* expert_idx
                  int32_t* expert_count, int32_t* slot_token, void* x_e, void* ws, void* stream);
 
 /* Step 4, expert FFN.  Switch notes 2.1 (one FFN E_i per expert):
- * y_e[e, s] = act(x_e[e, s] W1_e) W2_e for s < expert_count[e], with
- * W1_e = w1[e]^T and W2_e = w2[e]^T.
+ * y_e[e, s] = H[e, s] W2_e for s < expert_count[e], W2_e = w2[e]^T, with the
+ * hidden activations H[e, s] = act(x_e[e, s] W1_e), W1_e = w1[e]^T, or, for the
+ * GLU activations (MosaicBERT review, methodology), H[e, s] = act(x_e[e, s] W_e)
+ * * (x_e[e, s] V_e) with W_e^T = w1[e][0 : d_ff] and V_e^T = w1[e][d_ff : 2 d_ff].
  *   x_e          [E, C, d_model] dtype (rows past the count are never read)
  *   expert_count [E] int32 (values above C are treated as C)
- *   w1           [E, d_ff, d_model] dtype (stored output x input)
+ *   w1           [E, d_ff, d_model] dtype (stored output x input);
+ *                GLU: [E, 2 * d_ff, d_model], the W rows then the V rows
  *   w2           [E, d_model, d_ff] dtype (stored output x input)
  *   y_e          [E, C, d_model] dtype out (rows past the count are not written)
- *   ws           workspace: the hidden activations act(x_e W1) in dtype.
- * bf16: matrix products on bf16 MFMA with float32 accumulation; the hidden
- * activation and y_e are rounded to bf16.  f32: float32 throughout. */
+ *   ws           workspace: the hidden activations H in dtype.
+ * bf16: matrix products on bf16 MFMA with float32 accumulation; H and y_e are
+ * rounded to bf16 (GLU: the gate product is formed in float32 from the two
+ * float32 accumulators, then rounded once).  f32: float32 throughout. */
 int moe_expert_ffn(const moe_config* cfg, const void* x_e, const int32_t* expert_count,
                    const void* w1, const void* w2, void* y_e, void* ws, void* stream);
 
 /* Step 4 in one launch, without the hidden activations in memory (bf16 only;
- * capacity 1..64, d_model a multiple of 384, d_ff a multiple of 128; otherwise
- * MOE_ERR_UNSUPPORTED).  Same arguments and results as moe_expert_ffn, bit for
+ * capacity 1..64, d_model a multiple of 384, d_ff a multiple of 128, ReLU or
+ * GELU; otherwise MOE_ERR_UNSUPPORTED).  Same arguments and results as moe_expert_ffn, bit for
  * bit (each hidden and output element is accumulated from the same bf16
  * products in the same order), and no workspace: per expert, d_ff is walked in
  * chunks of 128 whose activated hidden tile stays in on-chip memory and is
@@ -182,7 +191,8 @@ int moe_expert_ffn_fused(const moe_config* cfg, const void* x_e, const int32_t* 
                          const void* w1, const void* w2, void* y_e, void* stream);
 
 /* The two halves of step 4, for callers that keep the hidden activations:
- *   moe_expert_up:   hidden[e, s] = act(x_e[e, s] W1_e)   (one grouped GEMM launch)
+ *   moe_expert_up:   hidden[e, s] = H[e, s] as in moe_expert_ffn (one grouped GEMM
+ *                    launch; GLU: the gate product in its epilogue)
  *   moe_expert_down: y_e[e, s]    = hidden[e, s] W2_e     (one grouped GEMM launch)
  * for s < expert_count[e]; hidden is [E, C, d_ff] in dtype (caller-owned device
  * memory; rows past the count are not written / not read).  moe_expert_ffn is
@@ -218,7 +228,8 @@ int64_t moe_backward_workspace_bytes(const moe_config* cfg);
 /* Backward pass of the whole layer (training): gradients of a loss L through
  * y = sum over served choices c of p_{i_c}(x) E_{i_c}(x) (Switch notes 2.1,
  * Eq. 2; the gate keeps the router differentiable), E_i = act(x W1_i) W2_i and
- * p = softmax(W_r x + bias) (Eq. 1).  The chosen experts and the capacity drop
+ * p = softmax(W_r x + bias) (Eq. 1); for the GLU activations
+ * E_i = (act(x W_i) * (x V_i)) W2_i.  The chosen experts and the capacity drop
  * (2.2) are piecewise constant: no gradient flows through them and a dropped
  * choice contributes nothing.  Random routed experts have constant gates 1, so
  * the router gets no gradient (w_r, bias, dw_r, dbias are ignored).
@@ -229,12 +240,13 @@ int64_t moe_backward_workspace_bytes(const moe_config* cfg);
  *   dx    [T, d_model] dtype out: dL/dx (expert path plus router path)
  *   dw_r  [E, d_model] float32 out (learned routing): dL/dW_r
  *   dbias [E] float32 out or NULL: dL/dbias (the sum of dL/dh over tokens)
- *   dw1   [E, d_ff, d_model], dw2 [E, d_model, d_ff] dtype out: dL/dw1, dL/dw2
+ *   dw1   [E, d_ff, d_model] (GLU: [E, 2 * d_ff, d_model]), dw2 [E, d_model, d_ff]
+ *         dtype out: dL/dw1, dL/dw2
  *         (every element written; zero for experts that served no token)
  *   bws   workspace of moe_backward_workspace_bytes(cfg) bytes.
  * bf16: products on bf16 MFMA with float32 accumulation; dy_e = gate * dy, dZ,
- * dx_e and the outputs are rounded to bf16; the GELU pre-activation is
- * recomputed in bf16.  The router gradient is float32; its token contraction is
+ * dx_e and the outputs are rounded to bf16; the pre-activation (GELU, and both
+ * halves for GLU) is recomputed in bf16.  The router gradient is float32; its token contraction is
  * split into 64 ranges added in order, so repeated calls give identical bits. */
 int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
                  const void* w1, const void* w2, const void* dy, void* dx, float* dw_r,

@@ -38,8 +38,10 @@ def make_config(T: int, d_model: int, d_ff: int, E: int, k: int, capacity_factor
 
 
 def config_for(wl) -> MoeConfig:
-    """Configuration of a workload record (moe_workloads.Workload or alike)."""
-    return make_config(wl.T, wl.d_model, wl.d_ff, wl.E, wl.k, wl.capacity_factor, wl.act,
+    """Configuration of a workload record (moe_workloads.Workload or alike); a record
+    with a true ``glu`` field selects the GLU form of its activation."""
+    act = {"relu": "reglu", "gelu": "geglu"}[wl.act] if getattr(wl, "glu", False) else wl.act
+    return make_config(wl.T, wl.d_model, wl.d_ff, wl.E, wl.k, wl.capacity_factor, act,
                        wl.dtype, wl.route, wl.n_groups, wl.rre_seed)
 
 

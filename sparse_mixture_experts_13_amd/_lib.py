@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, -1, -2, -3
 DTYPE = {"f32": 0, "bf16": 1}
-ACT = {"relu": 0, "gelu": 1}
+ACT = {"relu": 0, "gelu": 1, "reglu": 2, "geglu": 3}
 ROUTE = {"topk": 0, "rre": 1}
 REGION = {"expert_idx": 0, "gate": 1, "slot": 2, "expert_count": 3, "slot_token": 4,
           "x_e": 5, "hidden": 6, "y_e": 7}

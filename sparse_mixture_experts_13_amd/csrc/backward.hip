@@ -13,6 +13,9 @@
 //   router: dp_e = sum of dgate over the choices of e, dh = p (dp - <p, dp>),
 //           dx += dh W_r, dw_r = dh^T x, dbias = sum_t dh
 //   dx[t] = sum over served choices of dx_e[e,s], plus the router term.
+// GLU experts (MosaicBERT review, methodology), H = act(Za) * Zb with
+// (Za, Zb) = x_e [W; V]^T: dZa = dH * Zb * act'(Za), dZb = dH * act(Za), and
+// dZ = (dZa, dZb) takes the place of dZ over the 2 f stacked rows of w1.
 //
 // gfx950 design.  Scatter, softmax-Jacobian and final gather are one wave per
 // token.  All four expert products run on one grouped GEMM kernel with operand
@@ -182,7 +185,10 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(
 // stores zeros (weight gradients of an expert with no tokens).
 // EPI 0: store bf16(acc).  EPI 1: bf16(acc * act'(z)) with z read from `aux`
 // at the output position (ACT 0: z is the hidden activation, act' = z > 0;
-// ACT 1: z is the pre-activation, act' = GELU derivative).
+// ACT 1: z is the pre-activation, act' = GELU derivative).  EPI 2 (GLU, acc =
+// dH): with za = aux[m][n] and zb = aux[m][N + n] (aux and out have row pitch
+// ldo = 2 N), stores bf16(acc * zb * act'(za)) at out[m][n] and
+// bf16(acc * act(za)) at out[m][N + n].
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ float gelu_grad(float z) {
@@ -325,49 +331,74 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
   // D[n][m]: lane holds m = fr and n = 8 * (r / 4) + 4 * half + r % 4 of each 32 x 32 tile.
   // The tile goes through LDS (the operand buffers are free after the last
   // barrier of the k loop), then out with 16-byte stores, four 256-byte row
-  // segments per wave instruction.
+  // segments per wave instruction.  EPI 2 makes two passes (dZa, then dZb).
   bf16_t* Oe = out + e * sOe;
   const bf16_t* Ze = aux ? aux + e * sOe : nullptr;
   bf16_t* st = smem_;  // [BM][OP]
+  auto unpack4 = [](uint2 zz, float* z) {
+    z[0] = __uint_as_float(zz.x << 16);
+    z[1] = __uint_as_float(zz.x & 0xFFFF0000u);
+    z[2] = __uint_as_float(zz.y << 16);
+    z[3] = __uint_as_float(zz.y & 0xFFFF0000u);
+  };
+  constexpr int NPASS = EPI == 2 ? 2 : 1;
 #pragma unroll
-  for (int t = 0; t < TM; ++t) {
-    const int ml = (wm * TM + t) * 32 + fr;
-    const int m = m0 + ml;
+  for (int pass = 0; pass < NPASS; ++pass) {
+    if (pass > 0) __syncthreads();  // the previous pass's staging reads are done
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const int nl0 = (wn * TN + i) * 32;
+    for (int t = 0; t < TM; ++t) {
+      const int ml = (wm * TM + t) * 32 + fr;
+      const int m = m0 + ml;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nl = nl0 + 8 * q + 4 * half;
-        float v[4];
+      for (int i = 0; i < TN; ++i) {
+        const int nl0 = (wn * TN + i) * 32;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = acc[i][t][4 * q + u];
-        if constexpr (EPI == 1) {
-          if (m < Mv && n0 + nl < N) {
-            const uint2 zz = *reinterpret_cast<const uint2*>(Ze + static_cast<int64_t>(m) * ldo + n0 + nl);
-            const float z[4] = {__uint_as_float(zz.x << 16), __uint_as_float(zz.x & 0xFFFF0000u),
-                                __uint_as_float(zz.y << 16), __uint_as_float(zz.y & 0xFFFF0000u)};
+        for (int q = 0; q < 4; ++q) {
+          const int nl = nl0 + 8 * q + 4 * half;
+          float v[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] *= ACT == 0 ? (z[u] > 0.f ? 1.f : 0.f) : gelu_grad(z[u]);
+          for (int u = 0; u < 4; ++u) v[u] = acc[i][t][4 * q + u];
+          if constexpr (EPI == 1) {
+            if (m < Mv && n0 + nl < N) {
+              float z[4];
+              unpack4(*reinterpret_cast<const uint2*>(Ze + static_cast<int64_t>(m) * ldo + n0 + nl), z);
+#pragma unroll
+              for (int u = 0; u < 4; ++u) v[u] *= ACT == 0 ? (z[u] > 0.f ? 1.f : 0.f) : gelu_grad(z[u]);
+            }
+          } else if constexpr (EPI == 2) {
+            if (m < Mv && n0 + nl < N) {
+              const bf16_t* zr = Ze + static_cast<int64_t>(m) * ldo + n0 + nl;
+              float za[4], zb[4];
+              unpack4(*reinterpret_cast<const uint2*>(zr), za);
+              unpack4(*reinterpret_cast<const uint2*>(zr + N), zb);
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                if (pass == 0)
+                  v[u] *= zb[u] * (ACT == 0 ? (za[u] > 0.f ? 1.f : 0.f) : gelu_grad(za[u]));
+                else
+                  v[u] *= apply_act<ACT>(za[u]);
+              }
+            }
           }
+          uint2 w;
+          w.x = pack_bf16x2(v[0], v[1]);
+          w.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(st + ml * OP + nl) = w;
         }
-        uint2 w;
-        w.x = pack_bf16x2(v[0], v[1]);
-        w.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(st + ml * OP + nl) = w;
       }
     }
-  }
-  __syncthreads();
-  constexpr int CPRow = BN / 8;  // 16-byte chunks per row
+    __syncthreads();
+    constexpr int CPRow = BN / 8;  // 16-byte chunks per row
+    bf16_t* Op = Oe + (pass ? N : 0);
 #pragma unroll
-  for (int it = 0; it < BM * CPRow / 256; ++it) {
-    const int q = it * 256 + tid;
-    const int ml = q / CPRow, c = q % CPRow;
-    const int m = m0 + ml, n = n0 + c * 8;
-    if (m < Mv && n < N)
-      *reinterpret_cast<u32x4*>(Oe + static_cast<int64_t>(m) * ldo + n) =
-          *reinterpret_cast<const u32x4*>(st + ml * OP + c * 8);
+    for (int it = 0; it < BM * CPRow / 256; ++it) {
+      const int q = it * 256 + tid;
+      const int ml = q / CPRow, c = q % CPRow;
+      const int m = m0 + ml, n = n0 + c * 8;
+      if (m < Mv && n < N)
+        *reinterpret_cast<u32x4*>(Op + static_cast<int64_t>(m) * ldo + n) =
+            *reinterpret_cast<const u32x4*>(st + ml * OP + c * 8);
+    }
   }
 }
 
@@ -457,6 +488,12 @@ __global__ __launch_bounds__(256) void fgemm_kernel(
       if constexpr (EPI == 1) {
         const float z = ld_f32(Ze + static_cast<int64_t>(m) * ldo + n);
         v *= ACT == 0 ? (z > 0.f ? 1.f : 0.f) : gelu_grad(z);
+      } else if constexpr (EPI == 2) {
+        // GLU: za at column n, zb at column N + n; dZb goes to column N + n
+        const float za = ld_f32(Ze + static_cast<int64_t>(m) * ldo + n);
+        const float zb = ld_f32(Ze + static_cast<int64_t>(m) * ldo + N + n);
+        st_f32(Oe + static_cast<int64_t>(m) * ldo + N + n, v * apply_act<ACT>(za));
+        v *= zb * (ACT == 0 ? (za > 0.f ? 1.f : 0.f) : gelu_grad(za));
       }
       st_f32(Oe + static_cast<int64_t>(m) * ldo + n, v);
     }
@@ -538,7 +575,17 @@ static hipError_t run_fgemm(int batch, int64_t C, const TA* A, int64_t sAe, int 
   } while (0)
 
 // Expert-side products for one dtype.  dZ is staged in the dZ buffer, the
-// pre-activation (GELU) in the Z buffer.
+// pre-activation (GELU) in the Z buffer.  GLU: Z = x_e [W; V]^T over the 2 f
+// stacked rows in the Z buffer ([C][2 f] per expert), dZ = (dZa, dZb) likewise,
+// and the products with w1 run over 2 f rows.
+
+// Plan of the plain product x_e . w1^T over every row of w1 (no activation).
+static Plan stacked_plan(const Plan& p) {
+  Plan q = p;
+  q.f = p.w1_rows();
+  q.glu = false;
+  return q;
+}
 template <typename T>
 static hipError_t expert_backward(const Plan& p, const T* x_e, const T* hidden, const T* w1,
                                   const T* w2, const int32_t* count, const T* dy_e, T* zbuf,
@@ -550,27 +597,37 @@ hipError_t expert_backward<bf16_t>(const Plan& p, const bf16_t* x_e, const bf16_
                                    const bf16_t* dy_e, bf16_t* zbuf, bf16_t* dz, bf16_t* dx_e,
                                    bf16_t* dw1, bf16_t* dw2, hipStream_t s) {
   const int d = static_cast<int>(p.d), f = static_cast<int>(p.f);
+  const int r = static_cast<int>(p.w1_rows());  // rows of w1: f, or 2 f for GLU
   const int64_t C = p.C, sX = C * d, sH = C * f, sW = int64_t(d) * f;
+  const int64_t sZ = C * r, sW1 = int64_t(d) * r;
   const int Ci = static_cast<int>(C);
-  // GELU: pre-activation Z = x_e . w1^T again (the forward keeps only act(Z))
-  if (p.act == 1) MOE_TRY(launch_expert_up_act(p, x_e, count, w1, zbuf, 2, s));
-  const bf16_t* z = p.act == 1 ? zbuf : hidden;
+  // GELU and GLU: pre-activation Z = x_e . w1^T again (the forward keeps only H)
+  if (p.act == 1 || p.glu) MOE_TRY(launch_expert_up_act(stacked_plan(p), x_e, count, w1, zbuf, 2, s));
+  const bf16_t* z = (p.act == 1 || p.glu) ? zbuf : hidden;
   // dZ[s][f] = sum_d dy_e[s][d] w2[d][f] * act'(Z)   (A = dy_e k-contiguous, B = w2 [k=d][n=f])
-  if (p.act == 0)
+  if (p.glu) {
+    if (p.act == 0)
+      MOE_TRY((run_bgemm<64, 128, 64, true, false, 2, 0>(p, dy_e, sX, d, w2, sW, f, dz, sZ, r, z, count, Ci,
+                                                      f, d, true, s)));
+    else
+      MOE_TRY((run_bgemm<64, 128, 64, true, false, 2, 1>(p, dy_e, sX, d, w2, sW, f, dz, sZ, r, z, count, Ci,
+                                                      f, d, true, s)));
+  } else if (p.act == 0) {
     MOE_TRY((run_bgemm<64, 128, 64, true, false, 1, 0>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
                                                     f, d, true, s)));
-  else
+  } else {
     MOE_TRY((run_bgemm<64, 128, 64, true, false, 1, 1>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
                                                     f, d, true, s)));
-  // dx_e[s][d] = sum_f dZ[s][f] w1[f][d]   (B = w1 [k=f][n=d])
-  MOE_TRY((run_bgemm<64, 128, 64, true, false, 0, 0>(p, dz, sH, f, w1, sW, d, dx_e, sX, d, nullptr, count,
-                                                  Ci, d, f, true, s)));
+  }
+  // dx_e[s][d] = sum_r dZ[s][r] w1[r][d]   (B = w1 [k=r][n=d])
+  MOE_TRY((run_bgemm<64, 128, 64, true, false, 0, 0>(p, dz, sZ, r, w1, sW1, d, dx_e, sX, d, nullptr, count,
+                                                  Ci, d, r, true, s)));
   // dw2[d][f] = sum_s dy_e[s][d] H[s][f]   (A = dy_e [k=s][m=d], B = H [k=s][n=f])
   MOE_TRY((run_bgemm<128, 128, 32, false, false, 0, 0>(p, dy_e, sX, d, hidden, sH, f, dw2, sW, f, nullptr,
                                                     count, d, f, 0, false, s)));
-  // dw1[f][d] = sum_s dZ[s][f] x_e[s][d]
-  MOE_TRY((run_bgemm<128, 128, 32, false, false, 0, 0>(p, dz, sH, f, x_e, sX, d, dw1, sW, d, nullptr, count,
-                                                    f, d, 0, false, s)));
+  // dw1[r][d] = sum_s dZ[s][r] x_e[s][d]
+  MOE_TRY((run_bgemm<128, 128, 32, false, false, 0, 0>(p, dz, sZ, r, x_e, sX, d, dw1, sW1, d, nullptr, count,
+                                                    r, d, 0, false, s)));
   return hipSuccess;
 }
 
@@ -580,22 +637,32 @@ hipError_t expert_backward<float>(const Plan& p, const float* x_e, const float* 
                                   const float* dy_e, float* zbuf, float* dz, float* dx_e, float* dw1,
                                   float* dw2, hipStream_t s) {
   const int d = static_cast<int>(p.d), f = static_cast<int>(p.f);
+  const int r = static_cast<int>(p.w1_rows());
   const int64_t C = p.C, sX = C * d, sH = C * f, sW = int64_t(d) * f;
+  const int64_t sZ = C * r, sW1 = int64_t(d) * r;
   const int Ci = static_cast<int>(C);
-  if (p.act == 1) MOE_TRY(launch_expert_up_act(p, x_e, count, w1, zbuf, 2, s));
-  const float* z = p.act == 1 ? zbuf : hidden;
-  if (p.act == 0)
+  if (p.act == 1 || p.glu) MOE_TRY(launch_expert_up_act(stacked_plan(p), x_e, count, w1, zbuf, 2, s));
+  const float* z = (p.act == 1 || p.glu) ? zbuf : hidden;
+  if (p.glu) {
+    if (p.act == 0)
+      MOE_TRY((run_fgemm<float, float, float, true, false, 2, 0>(p.E, C, dy_e, sX, d, w2, sW, f, dz, sZ, 0,
+                                                                  r, z, count, Ci, f, d, true, 1, s)));
+    else
+      MOE_TRY((run_fgemm<float, float, float, true, false, 2, 1>(p.E, C, dy_e, sX, d, w2, sW, f, dz, sZ, 0,
+                                                                  r, z, count, Ci, f, d, true, 1, s)));
+  } else if (p.act == 0) {
     MOE_TRY((run_fgemm<float, float, float, true, false, 1, 0>(p.E, C, dy_e, sX, d, w2, sW, f, dz, sH, 0,
                                                                 f, z, count, Ci, f, d, true, 1, s)));
-  else
+  } else {
     MOE_TRY((run_fgemm<float, float, float, true, false, 1, 1>(p.E, C, dy_e, sX, d, w2, sW, f, dz, sH, 0,
                                                                 f, z, count, Ci, f, d, true, 1, s)));
-  MOE_TRY((run_fgemm<float, float, float, true, false, 0, 0>(p.E, C, dz, sH, f, w1, sW, d, dx_e, sX, 0, d,
-                                                              nullptr, count, Ci, d, f, true, 1, s)));
+  }
+  MOE_TRY((run_fgemm<float, float, float, true, false, 0, 0>(p.E, C, dz, sZ, r, w1, sW1, d, dx_e, sX, 0, d,
+                                                              nullptr, count, Ci, d, r, true, 1, s)));
   MOE_TRY((run_fgemm<float, float, float, false, false, 0, 0>(p.E, C, dy_e, sX, d, hidden, sH, f, dw2, sW,
                                                                0, f, nullptr, count, d, f, 0, false, 1, s)));
-  MOE_TRY((run_fgemm<float, float, float, false, false, 0, 0>(p.E, C, dz, sH, f, x_e, sX, d, dw1, sW, 0,
-                                                               d, nullptr, count, f, d, 0, false, 1, s)));
+  MOE_TRY((run_fgemm<float, float, float, false, false, 0, 0>(p.E, C, dz, sZ, r, x_e, sX, d, dw1, sW1, 0,
+                                                               d, nullptr, count, r, d, 0, false, 1, s)));
   return hipSuccess;
 }
 
@@ -619,8 +686,9 @@ static hipError_t backward_typed(const Plan& p, const BwdArgs& a, hipStream_t s)
   else {
     // no capacity: every weight gradient is zero (sizes are multiples of 64 elements)
     const int64_t n16 = int64_t(p.E) * p.d * p.f * p.elem / 16;
-    const unsigned g = static_cast<unsigned>(std::min<int64_t>((n16 + 255) / 256, 4096));
-    hipLaunchKernelGGL(zero_fill_kernel, dim3(g), dim3(256), 0, s, static_cast<u32x4*>(a.dw1), n16);
+    const int64_t n16w1 = int64_t(p.E) * p.d * p.w1_rows() * p.elem / 16;
+    const unsigned g = static_cast<unsigned>(std::min<int64_t>((n16w1 + 255) / 256, 4096));
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(g), dim3(256), 0, s, static_cast<u32x4*>(a.dw1), n16w1);
     hipLaunchKernelGGL(zero_fill_kernel, dim3(g), dim3(256), 0, s, static_cast<u32x4*>(a.dw2), n16);
     MOE_TRY(hipGetLastError());
   }
@@ -740,13 +808,13 @@ __global__ __launch_bounds__(256) void clip_scale_kernel(T* __restrict__ p, int6
 template <typename T>
 static hipError_t clip_typed(const Plan& p, float* dw_r, float* dbias, T* dw1, T* dw2,
                              double max_norm, float* nc, double* part, hipStream_t s) {
-  const int64_t nw = int64_t(p.E) * p.d * p.f;
+  const int64_t nw = int64_t(p.E) * p.d * p.f, nw1 = int64_t(p.E) * p.d * p.w1_rows();
   const int64_t nr = dw_r ? int64_t(p.E) * p.d : 0, nb = dbias ? p.E : 0;
   // empty arrays still write their (zero) partials
   hipLaunchKernelGGL(clip_sumsq_kernel<float>, dim3(kClipBlocks), dim3(256), 0, s, dw_r, nr, part);
   hipLaunchKernelGGL(clip_sumsq_kernel<float>, dim3(kClipBlocks), dim3(256), 0, s, dbias, nb,
                      part + kClipBlocks);
-  hipLaunchKernelGGL(clip_sumsq_kernel<T>, dim3(kClipBlocks), dim3(256), 0, s, dw1, nw,
+  hipLaunchKernelGGL(clip_sumsq_kernel<T>, dim3(kClipBlocks), dim3(256), 0, s, dw1, nw1,
                      part + 2 * kClipBlocks);
   hipLaunchKernelGGL(clip_sumsq_kernel<T>, dim3(kClipBlocks), dim3(256), 0, s, dw2, nw,
                      part + 3 * kClipBlocks);
@@ -754,7 +822,7 @@ static hipError_t clip_typed(const Plan& p, float* dw_r, float* dbias, T* dw1, T
   const unsigned g = 2048;
   if (nr) hipLaunchKernelGGL(clip_scale_kernel<float>, dim3(g), dim3(256), 0, s, dw_r, nr, nc);
   if (nb) hipLaunchKernelGGL(clip_scale_kernel<float>, dim3(1), dim3(256), 0, s, dbias, nb, nc);
-  hipLaunchKernelGGL(clip_scale_kernel<T>, dim3(g), dim3(256), 0, s, dw1, nw, nc);
+  hipLaunchKernelGGL(clip_scale_kernel<T>, dim3(g), dim3(256), 0, s, dw1, nw1, nc);
   hipLaunchKernelGGL(clip_scale_kernel<T>, dim3(g), dim3(256), 0, s, dw2, nw, nc);
   return hipGetLastError();
 }

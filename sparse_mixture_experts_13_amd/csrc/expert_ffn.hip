@@ -12,6 +12,16 @@
 // grid is fixed (no device-to-host read of the counts) while dropped or unused
 // capacity costs neither bandwidth nor MFMA work.  float32 workloads use a
 // plain float32 FMA tile kernel.
+//
+// Gated-linear-unit experts (MosaicBERT review, methodology: GLU in the
+// feed-forward layer, in a fused form): H = act(x W) * (x V) with w1 = [W; V]
+// stacked (2 d_ff rows).  The up-projection is one grouped GEMM over the 2 d_ff
+// rows in a permuted row order: virtual weight row v is physical row
+// glu_row(v), so that every 32-row MFMA tile holds 16 units of W followed by the
+// same 16 units of V.  Each lane then holds both halves of its units in its own
+// accumulators (rows 8q + 4h + u and 16 + 8q + 4h + u), and the epilogue writes
+// act(a) * b once, in bfloat16 from the float32 accumulators: no pre-activation
+// reaches memory and no second pass runs.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -22,6 +32,12 @@ namespace moe {
 constexpr int GBK = 64;
 constexpr int GLD = GBK + 8;
 
+// Physical w1 row of virtual row v of the GLU up-projection (f = d_ff): 32-row
+// groups of 16 rows of W (rows 0 .. f - 1) and the same 16 units of V (rows f ..).
+__device__ __forceinline__ int glu_row(int v, int f) {
+  return ((v & 16) ? f : 0) + ((v >> 5) << 4) + (v & 15);
+}
+
 template <int BM, int BN>
 __host__ __device__ constexpr int ffn_lds_bytes() {
   return 2 * (BM + BN) * GLD * 2;
@@ -31,7 +47,7 @@ __host__ __device__ constexpr int ffn_lds_bytes() {
 // tile, column tile) of BM x BN, register-staged double-buffered LDS tiles
 // (BK = 64, rows padded to 144 bytes: conflict-free fragment reads); tiles past
 // the expert's count exit at once.
-template <int BM, int BN, int WM, int WN, int ACT>
+template <int BM, int BN, int WM, int WN, int ACT, bool GLU>
 __global__ __launch_bounds__(256) void ffn_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
     const int32_t* __restrict__ count, int64_t C, int N, int K, int n_mt, int n_nt) {
@@ -60,7 +76,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16_kernel(
   const int n0 = nt * BN;
 
   const bf16_t* Ae = A + (static_cast<int64_t>(e) * C + m0) * K;
-  const bf16_t* We = W + (static_cast<int64_t>(e) * N + n0) * K;
+  const bf16_t* We = W + static_cast<int64_t>(e) * N * K;
 
   u32x4 rq[QL], rp[PL];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -74,7 +90,8 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
       const int cid = tid + 256 * i, r = cid >> 3, c = cid & 7;
-      rp[i] = n0 + r < N ? *reinterpret_cast<const u32x4*>(We + static_cast<int64_t>(r) * K + k0 + c * 8)
+      const int wr = GLU ? glu_row(n0 + r, N >> 1) : n0 + r;
+      rp[i] = n0 + r < N ? *reinterpret_cast<const u32x4*>(We + static_cast<int64_t>(wr) * K + k0 + c * 8)
                          : zero4;
     }
   };
@@ -130,6 +147,35 @@ __global__ __launch_bounds__(256) void ffn_gemm_bf16_kernel(
 
   // D[n][m] of each 32x32 tile: lane holds m = lane % 32 and, for accumulator
   // element r, n = 8*(r/4) + 4*(lane/32) + r%4: four consecutive columns per group.
+  if constexpr (GLU) {
+    // GLU: elements 4g + u (g = 0, 1) hold the W half of unit 8g + 4h + u of the
+    // tile's 16 units, elements 4g + 8 + u the V half of the same unit
+    const int No = N >> 1;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int m = m0 + wm * WTM + j * 32 + fr;
+      if (m < cnt) {
+        bf16_t* orow = out + (static_cast<int64_t>(e) * C + m) * No;
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const int nt = n0 + wn * WTN + i * 32;
+          if (nt < N) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              float h[4];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) h[u] = apply_act<ACT>(acc[i][j][4 * g + u]) * acc[i][j][4 * g + 8 + u];
+              uint2 v;
+              v.x = pack_bf16x2(h[0], h[1]);
+              v.y = pack_bf16x2(h[2], h[3]);
+              *reinterpret_cast<uint2*>(orow + (nt >> 1) + 8 * g + 4 * (lane >> 5)) = v;
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     const int m = m0 + wm * WTM + j * 32 + fr;
@@ -183,7 +229,7 @@ __host__ __device__ constexpr int ffn_ring_lds_bytes() {
   return S * (WN * TN * 32 + WM * TM * 32) * BK * 2 + (kMaxE + 1) * 4;
 }
 
-template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT>
+template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT, bool GLU>
 __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
     const int32_t* __restrict__ count, int E, int64_t C, int N, int K) {
@@ -272,7 +318,9 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
       const int p = (wave * WL + q) * 64 + lane;
       const int row = p / CPR;
       const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
-      const uint32_t off = static_cast<uint32_t>(min(lc.nb * BN + row, N - 1)) * K + lk * BK + c * 8;
+      int wr = min(lc.nb * BN + row, N - 1);
+      if constexpr (GLU) wr = glu_row(wr, N >> 1);
+      const uint32_t off = static_cast<uint32_t>(wr) * K + lk * BK + c * 8;
       // non-temporal when each weight tile is read by one row block only
       __builtin_amdgcn_global_load_lds(We + off, (lds_void*)(base + (wave * WL + q) * 1024), 16, 0,
                                        NTW ? 2 : 0);
@@ -364,7 +412,27 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const int m = m0 + (wm * TM + t) * 32 + fr;
-      if (m < cc.cnt) {
+      if (GLU && m < cc.cnt) {
+        // elements 4q + u (q = 0, 1): W half of unit 8q + 4h + u of the 32-row
+        // tile's 16 units; elements 4q + 8 + u: the V half of the same unit
+        bf16_t* orow = out + (static_cast<int64_t>(cc.e) * C + m) * (N >> 1);
+#pragma unroll
+        for (int i = 0; i < TN; ++i) {
+          const int nt0 = n0 + (wn * TN + i) * 32;
+          if (nt0 < N) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              float h[4];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) h[u] = apply_act<ACT>(acc[i][t][4 * q + u]) * acc[i][t][4 * q + 8 + u];
+              uint2 v;
+              v.x = pack_bf16x2(h[0], h[1]);
+              v.y = pack_bf16x2(h[2], h[3]);
+              *reinterpret_cast<uint2*>(orow + (nt0 >> 1) + 8 * q + 4 * half) = v;
+            }
+          }
+        }
+      } else if (m < cc.cnt) {
         bf16_t* orow = out + (static_cast<int64_t>(cc.e) * C + m) * N;
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
@@ -631,7 +699,7 @@ __global__ __launch_bounds__(512) void ffn_fused_bf16_kernel(
 }
 
 // float32 grouped GEMM: 64 x 64 tile, 4 x 4 outputs per thread, BK = 16.
-template <int ACT>
+template <int ACT, bool GLU>
 __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(const float* __restrict__ A,
                                                            const float* __restrict__ W,
                                                            float* __restrict__ out,
@@ -653,7 +721,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(const float* __restri
   const int m0 = mt * 64, n0 = nt * 64;
   if (m0 >= cnt) return;
   const float* Ae = A + (static_cast<int64_t>(e) * C + m0) * K;
-  const float* We = W + (static_cast<int64_t>(e) * N + n0) * K;
+  const float* We = W + static_cast<int64_t>(e) * N * K;
   const int ty = tid >> 4, tx = tid & 15;
   float acc[4][4];
 #pragma unroll
@@ -665,7 +733,8 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(const float* __restri
     for (int i = 0; i < 4; ++i) {
       const int q = tid + 256 * i, r = q >> 4, c = q & 15;
       sA[r][c] = m0 + r < cnt ? Ae[static_cast<int64_t>(r) * K + k0 + c] : 0.f;
-      sB[r][c] = n0 + r < N ? We[static_cast<int64_t>(r) * K + k0 + c] : 0.f;
+      const int wr = GLU ? glu_row(n0 + r, N >> 1) : n0 + r;
+      sB[r][c] = n0 + r < N ? We[static_cast<int64_t>(wr) * K + k0 + c] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -686,19 +755,29 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(const float* __restri
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty + 16 * i;
     if (m < cnt) {
+      if constexpr (GLU) {
+        // virtual columns n0 + tx + 16 j: j = 0, 2 the W half and j = 1, 3 the V
+        // half of units n0 / 2 + tx and n0 / 2 + 16 + tx (N is a multiple of 64)
+        float* orow = out + (static_cast<int64_t>(e) * C + m) * (N >> 1) + (n0 >> 1) + tx;
+        if (n0 < N) {
+          orow[0] = apply_act<ACT>(acc[i][0]) * acc[i][1];
+          orow[16] = apply_act<ACT>(acc[i][2]) * acc[i][3];
+        }
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + tx + 16 * j;
-        if (n < N) out[(static_cast<int64_t>(e) * C + m) * N + n] = apply_act<ACT>(acc[i][j]);
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + tx + 16 * j;
+          if (n < N) out[(static_cast<int64_t>(e) * C + m) * N + n] = apply_act<ACT>(acc[i][j]);
+        }
       }
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN, int ACT>
+template <int BM, int BN, int WM, int WN, int ACT, bool GLU>
 static hipError_t run_bf16(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
                            const int32_t* count, int64_t C, int N, int K, hipStream_t s) {
-  auto kern = ffn_gemm_bf16_kernel<BM, BN, WM, WN, ACT>;
+  auto kern = ffn_gemm_bf16_kernel<BM, BN, WM, WN, ACT, GLU>;
   constexpr int lds = ffn_lds_bytes<BM, BN>();
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -712,10 +791,10 @@ static hipError_t run_bf16(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
   return hipGetLastError();
 }
 
-template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT>
+template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT, bool GLU>
 static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
                            const int32_t* count, int64_t C, int N, int K, hipStream_t s) {
-  auto kern = ffn_ring_bf16_kernel<TM, TN, WM, WN, S, BK, NTW, ACT>;
+  auto kern = ffn_ring_bf16_kernel<TM, TN, WM, WN, S, BK, NTW, ACT, GLU>;
   constexpr int lds = ffn_ring_lds_bytes<TM, TN, WM, WN, S, BK>();
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -745,14 +824,14 @@ static hipError_t run_fused(const Plan& p, int nspl, const bf16_t* A, const bf16
   return hipGetLastError();
 }
 
-template <int ACT>
+template <int ACT, bool GLU = false>
 static hipError_t run_f32(int E, const float* A, const float* W, float* out, const int32_t* count,
                           int64_t C, int N, int K, hipStream_t s) {
   const int n_mt = static_cast<int>((C + 63) / 64);
   const int n_nt = (N + 63) / 64;
   const int64_t nblk = static_cast<int64_t>(E) * n_mt * n_nt;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL(ffn_gemm_f32_kernel<ACT>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s,
+  hipLaunchKernelGGL((ffn_gemm_f32_kernel<ACT, GLU>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s,
                      A, W, out, count, C, N, K, n_mt, n_nt);
   return hipGetLastError();
 }
@@ -767,17 +846,22 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // 4 x 2 MFMA tiles, 2-stage ring of 64 KB stages; each weight tile is read by
 // every 256-row block of its expert, so those loads stay temporal).  Capacity
 // 161..384: the LDS-tiled 128 x 128 kernel, which wastes less on a partly
-// filled last row block (measured at capacity 320).
-template <int ACT>
+// filled last row block (measured at capacity 320).  The ring kernel addresses
+// inside one expert with 32-bit offsets; larger experts take the LDS-tiled one.
+// N is the number of weight rows (2 d_ff for the GLU up-projection).
+template <int ACT, bool GLU = false>
 static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf16_t* out,
                             const int32_t* count, int N, int K, hipStream_t s) {
-  if (p.C > 384) return run_ring<4, 2, 2, 4, 2, 64, false, ACT>(p.E, A, W, out, count, p.C, N, K, s);
+  const int64_t lim = int64_t(1) << 32;
+  if (int64_t(N) * K >= lim || p.C * K >= lim)
+    return run_bf16<128, 128, 2, 2, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C > 384) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
-    return run_ring<2, 3, 1, 4, 2, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C <= 128) return run_ring<4, 1, 1, 8, 3, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C <= 160) return run_ring<5, 2, 1, 4, 3, 64, true, ACT>(p.E, A, W, out, count, p.C, N, K, s);
-  return run_bf16<128, 128, 2, 2, ACT>(p.E, A, W, out, count, p.C, N, K, s);
+    return run_ring<2, 3, 1, 4, 2, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C <= 128) return run_ring<4, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C <= 160) return run_ring<5, 2, 1, 4, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  return run_bf16<128, 128, 2, 2, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
 }
 
 // Column groups per expert for the fused FFN, or 0 where it does not apply:
@@ -785,7 +869,7 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
 // split into column groups of 384 (NH = 2: 64 accumulator registers per lane;
 // wider groups spill).
 int fused_ffn_split(const Plan& p) {
-  if (p.dtype != 1 || p.C > 64 || p.C < 1 || p.f % kFusedFC != 0 || p.d % 384 != 0) return 0;
+  if (p.glu || p.dtype != 1 || p.C > 64 || p.C < 1 || p.f % kFusedFC != 0 || p.d % 384 != 0) return 0;
   if (p.d * p.f >= (int64_t(1) << 31)) return 0;  // 32-bit offsets inside one expert
   return static_cast<int>(p.d / 384);
 }
@@ -811,12 +895,18 @@ hipError_t launch_expert_up(const Plan& p, const void* x_e, const int32_t* exper
     const bf16_t* xe = static_cast<const bf16_t*>(x_e);
     const bf16_t* w = static_cast<const bf16_t*>(w1);
     bf16_t* h = static_cast<bf16_t*>(hidden);
+    if (p.glu)
+      return p.act == 0 ? gemm_bf16<0, true>(p, xe, w, h, expert_count, 2 * f, d, s)
+                        : gemm_bf16<1, true>(p, xe, w, h, expert_count, 2 * f, d, s);
     return p.act == 0 ? gemm_bf16<0>(p, xe, w, h, expert_count, f, d, s)
                       : gemm_bf16<1>(p, xe, w, h, expert_count, f, d, s);
   }
   const float* xe = static_cast<const float*>(x_e);
   const float* w = static_cast<const float*>(w1);
   float* h = static_cast<float*>(hidden);
+  if (p.glu)
+    return p.act == 0 ? run_f32<0, true>(p.E, xe, w, h, expert_count, p.C, 2 * f, d, s)
+                      : run_f32<1, true>(p.E, xe, w, h, expert_count, p.C, 2 * f, d, s);
   return p.act == 0 ? run_f32<0>(p.E, xe, w, h, expert_count, p.C, f, d, s)
                     : run_f32<1>(p.E, xe, w, h, expert_count, p.C, f, d, s);
 }

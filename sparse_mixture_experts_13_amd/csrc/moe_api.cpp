@@ -59,8 +59,8 @@ int validate(const moe_config* cfg) {
     return fail(MOE_ERR_ARG, "capacity_factor must be finite and > 0");
   if (cfg->dtype != MOE_DTYPE_F32 && cfg->dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_ARG, "dtype must be MOE_DTYPE_F32 or MOE_DTYPE_BF16");
-  if (cfg->act != MOE_ACT_RELU && cfg->act != MOE_ACT_GELU)
-    return fail(MOE_ERR_ARG, "act must be MOE_ACT_RELU or MOE_ACT_GELU");
+  if (cfg->act < MOE_ACT_RELU || cfg->act > MOE_ACT_GEGLU)
+    return fail(MOE_ERR_ARG, "act must be MOE_ACT_RELU, MOE_ACT_GELU, MOE_ACT_REGLU or MOE_ACT_GEGLU");
   if (cfg->route != MOE_ROUTE_TOPK && cfg->route != MOE_ROUTE_RRE)
     return fail(MOE_ERR_ARG, "route must be MOE_ROUTE_TOPK or MOE_ROUTE_RRE");
   if (cfg->route == MOE_ROUTE_RRE) {
@@ -100,7 +100,8 @@ void make_plan(const moe_config* cfg, moe::Plan& p) {
   }
   p.NB = static_cast<int>((cfg->T + p.TB - 1) / p.TB);
   p.dtype = cfg->dtype;
-  p.act = cfg->act;
+  p.act = (cfg->act == MOE_ACT_GELU || cfg->act == MOE_ACT_GEGLU) ? 1 : 0;
+  p.glu = cfg->act == MOE_ACT_REGLU || cfg->act == MOE_ACT_GEGLU;
   p.route = cfg->route;
   p.n_groups = cfg->n_groups;
   p.rre_seed = cfg->rre_seed;
@@ -146,8 +147,9 @@ void bwd_layout(const moe::Plan& p, BwdLayout& L) {
   L.gate = take(Tk * 4);
   L.dgate = take(Tk * 4);
   L.dy_e = take(EC * p.d * p.elem);
-  L.zbuf = take(p.act == MOE_ACT_GELU ? EC * p.f * p.elem : 0);
-  L.dz = take(EC * p.f * p.elem);
+  // pre-activations recomputed for act': GELU, and both halves for GLU
+  L.zbuf = take(p.glu ? EC * 2 * p.f * p.elem : (p.act == 1 ? EC * p.f * p.elem : 0));
+  L.dz = take(EC * p.w1_rows() * p.elem);
   L.dx_e = take(EC * p.d * p.elem);
   L.dh = take(topk ? p.T * p.Epad * 4 : 0);
   L.dx_r = take(topk ? p.T * p.d * 4 : 0);
@@ -292,7 +294,7 @@ int moe_expert_ffn(const moe_config* cfg, const void* x_e, const int32_t* expert
   const int64_t wbytes = int64_t(p.E) * p.d * p.f * p.elem;
   MOE_CHECK(need(x_e, EC * p.d * p.elem, "x_e"));
   MOE_CHECK(need(expert_count, int64_t(p.E) * 4, "expert_count"));
-  MOE_CHECK(need(w1, wbytes, "w1"));
+  MOE_CHECK(need(w1, wbytes / p.f * p.w1_rows(), "w1"));
   MOE_CHECK(need(w2, wbytes, "w2"));
   MOE_CHECK(need(y_e, EC * p.d * p.elem, "y_e"));
   MOE_CHECK(need(ws, p.total, "ws"));
@@ -309,13 +311,13 @@ int moe_expert_ffn_fused(const moe_config* cfg, const void* x_e, const int32_t* 
   const int nspl = moe::fused_ffn_split(p);
   if (nspl == 0)
     return fail(MOE_ERR_UNSUPPORTED,
-                "fused expert FFN needs bf16, 1 <= capacity <= 64, d_model % 384 == 0 and "
-                "d_ff % 128 == 0");
+                "fused expert FFN needs bf16, ReLU or GELU, 1 <= capacity <= 64, "
+                "d_model % 384 == 0 and d_ff % 128 == 0");
   const int64_t EC = int64_t(p.E) * p.C;
   const int64_t wbytes = int64_t(p.E) * p.d * p.f * p.elem;
   MOE_CHECK(need(x_e, EC * p.d * p.elem, "x_e"));
   MOE_CHECK(need(expert_count, int64_t(p.E) * 4, "expert_count"));
-  MOE_CHECK(need(w1, wbytes, "w1"));
+  MOE_CHECK(need(w1, wbytes / p.f * p.w1_rows(), "w1"));
   MOE_CHECK(need(w2, wbytes, "w2"));
   MOE_CHECK(need(y_e, EC * p.d * p.elem, "y_e"));
   MOE_HIP(moe::launch_expert_ffn_fused(p, nspl, x_e, expert_count, w1, w2, y_e,
@@ -332,7 +334,7 @@ int moe_expert_up(const moe_config* cfg, const void* x_e, const int32_t* expert_
   const int64_t EC = int64_t(p.E) * p.C;
   MOE_CHECK(need(x_e, EC * p.d * p.elem, "x_e"));
   MOE_CHECK(need(expert_count, int64_t(p.E) * 4, "expert_count"));
-  MOE_CHECK(need(w1, int64_t(p.E) * p.d * p.f * p.elem, "w1"));
+  MOE_CHECK(need(w1, int64_t(p.E) * p.d * p.w1_rows() * p.elem, "w1"));
   MOE_CHECK(need(hidden, EC * p.f * p.elem, "hidden"));
   MOE_HIP(moe::launch_expert_up(p, x_e, expert_count, w1, hidden, static_cast<hipStream_t>(stream)),
           "expert up-projection");
@@ -381,7 +383,7 @@ int moe_forward(const moe_config* cfg, const void* x, const float* w_r, const fl
   MOE_CHECK(need(x, p.T * p.d * p.elem, "x"));
   if (p.route == MOE_ROUTE_TOPK) MOE_CHECK(need(w_r, 1, "w_r"));
   else MOE_CHECK(need(group_id, p.T * 4, "group_id"));
-  MOE_CHECK(need(w1, wbytes, "w1"));
+  MOE_CHECK(need(w1, wbytes / p.f * p.w1_rows(), "w1"));
   MOE_CHECK(need(w2, wbytes, "w2"));
   MOE_CHECK(need(y, p.T * p.d * p.elem, "y"));
   MOE_CHECK(need(ws, p.total, "ws"));
@@ -430,11 +432,11 @@ int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const f
     MOE_CHECK(need(w_r, 1, "w_r"));
     MOE_CHECK(need(dw_r, int64_t(p.E) * p.d * 4, "dw_r"));
   }
-  MOE_CHECK(need(w1, wbytes, "w1"));
+  MOE_CHECK(need(w1, wbytes / p.f * p.w1_rows(), "w1"));
   MOE_CHECK(need(w2, wbytes, "w2"));
   MOE_CHECK(need(dy, tbytes, "dy"));
   MOE_CHECK(need(dx, tbytes, "dx"));
-  MOE_CHECK(need(dw1, wbytes, "dw1"));
+  MOE_CHECK(need(dw1, wbytes / p.f * p.w1_rows(), "dw1"));
   MOE_CHECK(need(dw2, wbytes, "dw2"));
   MOE_CHECK(need(ws, p.total, "ws"));
   MOE_CHECK(need(bws, L.total, "bws"));
@@ -484,7 +486,7 @@ int moe_sparse_clip(const moe_config* cfg, float* dw_r, float* dbias, void* dw1,
   BwdLayout L;
   bwd_layout(p, L);
   const int64_t wbytes = int64_t(p.E) * p.d * p.f * p.elem;
-  MOE_CHECK(need(dw1, wbytes, "dw1"));
+  MOE_CHECK(need(dw1, wbytes / p.f * p.w1_rows(), "dw1"));
   MOE_CHECK(need(dw2, wbytes, "dw2"));
   MOE_CHECK(need(norm_coef, 8, "norm_coef"));
   MOE_CHECK(need(bws, L.total, "bws"));

@@ -16,9 +16,11 @@ struct Plan {
   int64_t T, d, f, C;
   int E, k, Epad, NB;      // Epad: E rounded up to 32; NB: router blocks of TB tokens
   int TB;                  // tokens per router block
-  int dtype, act, route, n_groups;
+  int dtype, act, route, n_groups;  // act: 0 ReLU, 1 GELU (the GLU forms set glu)
+  bool glu;                // gated-linear-unit FFN: w1 holds [W; V], 2 f rows
   uint64_t rre_seed;
   int elem;                // bytes per element of dtype
+  int64_t w1_rows() const { return glu ? 2 * f : f; }
   // workspace byte offsets
   int64_t off_region[8];
   int64_t off_hist, off_offsets, off_planes, off_flags, off_psum, total;

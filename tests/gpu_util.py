@@ -85,7 +85,7 @@ class Dev:
         """Generate and upload every expert's weights without a host-side stack."""
         wl = self.wl
         dt = elem_dtype(wl)
-        self.w1 = torch.empty((wl.E, wl.d_ff, wl.d_model), dtype=dt, device=DEV)
+        self.w1 = torch.empty((wl.E, W.w1_rows(wl), wl.d_model), dtype=dt, device=DEV)
         self.w2 = torch.empty((wl.E, wl.d_model, wl.d_ff), dtype=dt, device=DEV)
 
         def put(e, a, b):
@@ -136,7 +136,7 @@ class Dev:
         moe.forward(cfg, self.x, self.w_r, self.bias, self.group_id, self.w1, self.w2, y, self.ws)
         dy = to_dev(dy_host)
         out = {"dx": self.new((wl.T, wl.d_model), elem_dtype(wl)),
-               "dw1": self.new((wl.E, wl.d_ff, wl.d_model), elem_dtype(wl)),
+               "dw1": self.new((wl.E, W.w1_rows(wl), wl.d_model), elem_dtype(wl)),
                "dw2": self.new((wl.E, wl.d_model, wl.d_ff), elem_dtype(wl)),
                "dw_r": self.new((wl.E, wl.d_model), torch.float32) if wl.route == "topk" else None,
                "dbias": self.new((wl.E,), torch.float32) if (with_dbias and wl.route == "topk") else None}

@@ -106,6 +106,8 @@ BAD = [
     (dict(capacity_factor=float("inf")), "capacity_factor"),
     (dict(dtype=7), "dtype"),
     (dict(act=5), "act"),
+    (dict(act=4), "act"),
+    (dict(act=-1), "act"),
     (dict(route=3), "route"),
     (dict(route=1, k=2), "k == 1"),
     (dict(route=1, k=1, n_groups=3), "n_groups"),
@@ -186,6 +188,7 @@ def test_null_and_misaligned_pointers_rejected():
     (dict(d_model=320), "d_model % 384"),                       # 320 % 384 != 0
     (dict(d_model=384, d_ff=192), "d_ff % 128"),                # 192 % 128 != 0
     (dict(d_model=384, T=1000, E=8, k=1), "capacity <= 64"),    # C = 157
+    (dict(d_model=384, d_ff=256, act=3), "ReLU or GELU"),       # GLU
 ])
 def test_fused_ffn_rejects_unsupported_shapes(over, msg):
     lib = moe.load()
@@ -273,3 +276,20 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError, match="missing"):
         _lib.load()
+
+
+def test_glu_configs_accepted_and_sized():
+    """The GLU activations (REGLU 2, GEGLU 3) validate like their plain forms; the
+    forward workspace is unchanged (H has d_ff columns either way) and the backward
+    workspace grows by the second halves of the recomputed Z and of dZ."""
+    lib = moe.load()
+    for plain, glu in ((0, 2), (1, 3)):
+        a, b = _cfg(act=plain), _cfg(act=glu)
+        assert lib.moe_capacity(ctypes.byref(b)) == lib.moe_capacity(ctypes.byref(a)) > 0
+        assert lib.moe_workspace_bytes(ctypes.byref(b)) == lib.moe_workspace_bytes(ctypes.byref(a))
+        C = lib.moe_capacity(ctypes.byref(a))
+        half = 8 * C * 128 * 2                     # E * C * d_ff bf16 elements
+        zplain = half if plain == 1 else 0         # GELU keeps Z; ReLU reads H instead
+        grow = lib.moe_backward_workspace_bytes(ctypes.byref(b)) - \
+            lib.moe_backward_workspace_bytes(ctypes.byref(a))
+        assert 2 * half + half - zplain <= grow <= 2 * half + half - zplain + 2 * 256

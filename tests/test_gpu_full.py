@@ -30,9 +30,17 @@ def _sample(ref, T, rng, n=40):
     return np.array(sorted(picks))
 
 
-@pytest.mark.parametrize("name", list(W.WORKLOADS))
+# gated-linear-unit forms of two layer shapes (GELU gate: the GeGLU form)
+GLU_FULL = {
+    "switch_base_geglu_bf16": W.WORKLOADS["switch_base_bf16"].replace(name="switch_base_geglu_bf16",
+                                                                      act="gelu", glu=True),
+    "xmoe_top2_geglu_bf16": W.WORKLOADS["xmoe_top2_bf16"].replace(name="xmoe_top2_geglu_bf16", glu=True),
+}
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS) + list(GLU_FULL))
 def test_full_size_forward(name):
-    wl = W.WORKLOADS[name]
+    wl = W.WORKLOADS.get(name) or GLU_FULL[name]
     t0 = time.time()
     print(f"[gpu] full {name}: generating inputs", flush=True)
     inputs = W.make_inputs(wl, with_weights=False)
@@ -87,19 +95,20 @@ def test_full_size_router_aux(name):
     print(f"[gpu] full router aux {name}: loss {aux[0]:.6g}, rel err {err:.3g}", flush=True)
 
 
-def test_full_size_backward_switch_base():
-    """moe_backward on the Switch-Base layer against the oracle's float64 backward (all
-    gradients, every token and expert)."""
-    wl = W.WORKLOADS["switch_base_bf16"]
+@pytest.mark.parametrize("name", ["switch_base_bf16", "switch_base_geglu_bf16"])
+def test_full_size_backward_switch_base(name):
+    """moe_backward on the Switch-Base layer (plain and GeGLU experts) against the
+    oracle's float64 backward (all gradients, every token and expert)."""
+    wl = W.WORKLOADS.get(name) or GLU_FULL[name]
     t0 = time.time()
-    print("[gpu] full backward switch_base_bf16: inputs", flush=True)
+    print(f"[gpu] full backward {name}: inputs", flush=True)
     inputs = W.make_inputs(wl)
     dev = Dev(wl, inputs)
     dy = make_dy(wl)
     got = dev.run_backward(dy)
-    print(f"[gpu] full backward switch_base_bf16: oracle ({time.time() - t0:.1f}s)", flush=True)
+    print(f"[gpu] full backward {name}: oracle ({time.time() - t0:.1f}s)", flush=True)
     fwd = oracle.forward(wl, inputs)
     ref = oracle.backward(wl, inputs, fwd, oracle.as_f64(dy))
-    errs = check_backward(wl, got, ref, "switch_base_bf16")
-    print("[gpu] full backward switch_base_bf16: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items())
+    errs = check_backward(wl, got, ref, name)
+    print(f"[gpu] full backward {name}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items())
           + f" ({time.time() - t0:.1f}s)", flush=True)

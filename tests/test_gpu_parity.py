@@ -151,7 +151,8 @@ def test_backward_matches_oracle(name):
             assert torch.equal(val, again[key]), f"{key} differs between calls"
 
 
-@pytest.mark.parametrize("name", ["zipf_small_bf16", "rre_small_bf16", "tiny_switch_f32"])
+@pytest.mark.parametrize("name", ["zipf_small_bf16", "rre_small_bf16", "tiny_switch_f32", "geglu_top2_bf16",
+                                  "reglu_small_f32"])
 def test_sparse_clip(name):
     """moe_sparse_clip on the gradients moe_backward wrote: norm and coefficient against the
     oracle's SparseClip of the same gradient values, clipped values equal to each gradient
@@ -370,3 +371,24 @@ def test_rre_invalid_group_ids():
     inputs["group_id"][1::7] = -1
     ref, got = _run_case(wl, inputs, "rre bad groups")
     assert (got["expert_idx"].cpu().numpy()[::7] == -1).all()
+
+
+def test_glu_single_token_and_backward():
+    wl = BASE.replace(T=1, glu=True)
+    inputs = W.make_inputs(wl)
+    ref, _ = _run_case(wl, inputs, "GLU T=1")
+    dy = make_dy(wl)
+    want = oracle.backward(wl, inputs, ref, oracle.as_f64(dy))
+    check_backward(wl, Dev(wl, inputs).run_backward(dy), want, "GLU T=1 backward")
+
+
+def test_glu_backward_empty_input():
+    """No tokens: every gradient (dw1 over both stacked halves) is written as zero."""
+    wl = BASE.replace(T=0, glu=True)
+    print("[gpu] case GLU T=0 backward", flush=True)
+    dev = Dev(wl, W.make_inputs(wl))
+    got = dev.run_backward(make_dy(wl))
+    assert got["dw1"].shape == (wl.E, 2 * wl.d_ff, wl.d_model)
+    for key in ("dw1", "dw2", "dw_r", "dbias"):
+        if got[key] is not None:
+            assert not got[key].float().abs().max().item(), key
