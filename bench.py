@@ -102,10 +102,11 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     x, w_r, bias, gid = up(inputs["x"]), up(inputs["w_r"]), up(inputs["bias"]), up(inputs["group_id"])
-    w1 = torch.empty((wl.E, wl.d_ff, wl.d_model), dtype=elem, device=dev)
+    rows1 = W.w1_rows(wl)  # d_ff, or 2 d_ff stacked rows for GLU experts
+    w1 = torch.empty((wl.E, rows1, wl.d_model), dtype=elem, device=dev)
     w2 = torch.empty((wl.E, wl.d_model, wl.d_ff), dtype=elem, device=dev)
     keep_host = not args.no_cpu_baseline
-    host_w1 = np.empty((wl.E, wl.d_ff, wl.d_model), np.uint16 if es == 2 else np.float32) if keep_host else None
+    host_w1 = np.empty((wl.E, rows1, wl.d_model), np.uint16 if es == 2 else np.float32) if keep_host else None
     host_w2 = np.empty((wl.E, wl.d_model, wl.d_ff), np.uint16 if es == 2 else np.float32) if keep_host else None
 
     def put(e, a, b):
@@ -198,13 +199,33 @@ def main():
     kern_us["backward"] = timed(lambda: moe.backward(cfg, x, w_r, bias, w1, w2, dy_t, dx_t, dwr_t, dbias_t,
                                                      dw1_t, dw2_t, ws, bws, stream), max(2, R // 2))
     nc_t = torch.empty(2, dtype=torch.float32, device=dev)
-    kern_us["sparse_clip"] = timed(lambda: moe.sparse_clip(cfg, dwr_t, dbias_t, dw1_t, dw2_t, 1e30, nc_t, bws,
+    # SparseClip with clipping active (norm pass + in-place scale) and inactive (norm pass only)
+    kern_us["sparse_clip"] = timed(lambda: moe.sparse_clip(cfg, dwr_t, dbias_t, dw1_t, dw2_t, 1e-3, nc_t, bws,
                                                            stream), max(2, R // 2))
+    kern_us["sparse_clip_inactive"] = timed(lambda: moe.sparse_clip(cfg, dwr_t, dbias_t, dw1_t, dw2_t, 1e30, nc_t,
+                                                                    bws, stream), max(2, R // 2))
     del dw1_t, dw2_t, bws
     try:  # the single-launch FFN, where its shape conditions hold
         kern_us["ffn_fused"] = timed(lambda: moe.expert_ffn_fused(cfg, x_e, cnt_t, w1, w2, y_e, stream), R)
     except moe.MoeError:
         pass
+    if not wl.glu:
+        # GeGLU experts of the same shape (w1 of 2 d_ff rows, seeded N(0, 1/d_model)):
+        # the gated up-projection on the same dispatch, and the whole GeGLU layer's
+        # forward and backward
+        cfg_g = moe.config_for(wl.replace(act="gelu", glu=True))
+        gen = torch.Generator(device=dev).manual_seed(1)
+        w1g = (torch.randn((wl.E, 2 * wl.d_ff, wl.d_model), generator=gen, device=dev)
+               / wl.d_model ** 0.5).to(elem)
+        kern_us["glu_up"] = timed(lambda: moe.expert_up(cfg_g, x_e, cnt_t, w1g, hidden, stream), R)
+        ws_g = moe.alloc_workspace(cfg_g)
+        kern_us["glu_forward"] = timed(lambda: moe.forward(cfg_g, x, w_r, bias, gid, w1g, w2, y2, ws_g, stream), R)
+        dw1g, dw2g = torch.empty_like(w1g), torch.empty_like(w2)
+        bws_g = moe.alloc_backward_workspace(cfg_g, dev)
+        kern_us["glu_backward"] = timed(lambda: moe.backward(cfg_g, x, w_r, bias, w1g, w2, dy_t, dx_t, dwr_t,
+                                                             dbias_t, dw1g, dw2g, ws_g, bws_g, stream),
+                                        max(2, R // 2))
+        del w1g, dw1g, dw2g, bws_g, ws_g
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -213,14 +234,19 @@ def main():
     # algorithmic bytes / flops per launch (served rows only; weights of experts with tokens)
     d, f = wl.d_model, wl.d_ff
     wbytes = active * d * f * es
+    g1 = 2 if wl.glu else 1  # GLU: the up-projection reads and multiplies 2 d_ff weight rows
     algo = {
-        "gemm_up": dict(bytes=wbytes + served * d * es + served * f * es, flops=2.0 * served * d * f),
+        "gemm_up": dict(bytes=g1 * wbytes + served * d * es + served * f * es, flops=2.0 * g1 * served * d * f),
+        "glu_up": dict(bytes=2 * wbytes + served * d * es + served * f * es, flops=4.0 * served * d * f),
         "gemm_down": dict(bytes=wbytes + served * f * es + served * d * es, flops=2.0 * served * d * f),
         "router": dict(bytes=wl.T * d * es + (wl.E * d * 4 if wl.route == "topk" else wl.T * 4)
                        + 8 * wl.T * wl.k, flops=2.0 * wl.T * d * wl.E if wl.route == "topk" else 0.0),
         "combine": dict(bytes=served * d * es + 12 * wl.T * wl.k + wl.T * d * es, flops=0.0),
         "dispatch": dict(bytes=wl.T * d * es + served * d * es + 8 * wl.T * wl.k, flops=0.0),
         "ffn_fused": dict(bytes=2 * wbytes + 2 * served * d * es, flops=4.0 * served * d * f),
+        # all E experts' gradients: read for the norm, then read and written by the scale
+        "sparse_clip": dict(bytes=3 * wl.E * d * f * (g1 + 1) * es, flops=0.0),
+        "sparse_clip_inactive": dict(bytes=wl.E * d * f * (g1 + 1) * es, flops=0.0),
     }
     dom = max(("gemm_up", "gemm_down"), key=lambda n: kern_us[n])
     dom_us = kern_us[dom]
@@ -230,7 +256,7 @@ def main():
         bound, achieved, peak, unit = "mfma", algo[dom]["flops"] / dom_us / 1e6, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
         bound, achieved, peak, unit = "hbm", algo[dom]["bytes"] / dom_us / 1e3, HBM_PEAK_GBS, "GB/s"
-    kname = {"gemm_up": "grouped GEMM up-projection + act (moe_expert_up)",
+    kname = {"gemm_up": "grouped GEMM up-projection + act" + (" + GLU gate" if wl.glu else "") + " (moe_expert_up)",
              "gemm_down": "grouped GEMM down-projection (moe_expert_down)"}[dom]
     traffic = read_traffic(dom, wl.name)
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
@@ -267,12 +293,13 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded: dyadic x and router weight, N(0, 1/fan_in) expert weights)",
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d_model, "d_ff": wl.d_ff,
-                   "E": wl.E, "k": wl.k, "capacity_factor": wl.capacity_factor, "act": wl.act,
+                   "E": wl.E, "k": wl.k, "capacity_factor": wl.capacity_factor,
+                   "act": ({"relu": "reglu", "gelu": "geglu"}[wl.act] if wl.glu else wl.act),
                    "route": wl.route, "capacity": C, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "grouped_gemm_mfma_frac": round(2 * algo["gemm_up"]["flops"] /
+        "grouped_gemm_mfma_frac": round((algo["gemm_up"]["flops"] + algo["gemm_down"]["flops"]) /
                                         ((kern_us["gemm_up"] + kern_us["gemm_down"]) / 1e6) /
                                         (peak_flops * 1e12), 4),
         "served_assignments": served,

@@ -36,7 +36,7 @@ from typing import Callable, Optional
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "TEST_WORKLOADS", "get", "make_inputs",
+    "Workload", "WORKLOADS", "GLU_WORKLOADS", "TEST_WORKLOADS", "get", "make_inputs",
     "expert_weights", "w1_rows", "f32_to_bf16_bits", "bf16_bits_to_f32",
 ]
 
@@ -86,6 +86,13 @@ WORKLOADS = {
                                      dtype="bf16", zipf_s=1.1),
 }
 
+# Gated-linear-unit (GeGLU) forms of two layer shapes: w1 holds 2 * d_ff rows.
+GLU_WORKLOADS = {
+    "switch_base_geglu_bf16": WORKLOADS["switch_base_bf16"].replace(name="switch_base_geglu_bf16",
+                                                                    act="gelu", glu=True),
+    "xmoe_top2_geglu_bf16": WORKLOADS["xmoe_top2_bf16"].replace(name="xmoe_top2_geglu_bf16", glu=True),
+}
+
 # Reduced shapes of the same five kinds: small enough for the full oracle in
 # seconds, large enough to span several router blocks, several GEMM tiles and
 # ragged tails (T, counts and d_ff not multiples of the tile sizes).
@@ -124,8 +131,9 @@ TEST_WORKLOADS = {
 
 
 def get(name: str) -> Workload:
-    if name in WORKLOADS:
-        return WORKLOADS[name]
+    for table in (WORKLOADS, GLU_WORKLOADS):
+        if name in table:
+            return table[name]
     return TEST_WORKLOADS[name]
 
 

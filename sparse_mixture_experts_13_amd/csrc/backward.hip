@@ -222,12 +222,12 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
   bf16_t (*la)[TA::kElems] = reinterpret_cast<bf16_t (*)[TA::kElems]>(smem_);
   bf16_t (*lb)[TBt::kElems] = reinterpret_cast<bf16_t (*)[TBt::kElems]>(smem_ + 2 * TA::kElems);
 
-  const int e = blockIdx.z;
+  const int bx = blockIdx.x, by = blockIdx.y, e = blockIdx.z;
   int64_t cnt = count[e];
   cnt = cnt < 0 ? 0 : (cnt > C ? C : cnt);
   const int Mv = m_is_count ? static_cast<int>(cnt) : M;
   const int Kv = m_is_count ? K : static_cast<int>(cnt);
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int m0 = by * BM, n0 = bx * BN;
   if (m0 >= Mv) return;
   const bf16_t* Ae = A + e * sAe;
   const bf16_t* Be = B + e * sBe;
@@ -424,6 +424,7 @@ __global__ __launch_bounds__(256) void fgemm_kernel(
     const int32_t* __restrict__ count, int64_t C, int M, int N, int K, bool m_is_count, int KS) {
   __shared__ float sa[16][65];
   __shared__ float sb[16][65];
+  const int bx = blockIdx.x, by = blockIdx.y;
   const int e = blockIdx.z / KS, ks = blockIdx.z % KS;
   int Mv = M, Kv = K;
   if (count) {
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(256) void fgemm_kernel(
     if (m_is_count) Mv = static_cast<int>(cnt);
     else Kv = static_cast<int>(cnt);
   }
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int m0 = by * 64, n0 = bx * 64;
   if (m0 >= Mv) return;
   const int kb = static_cast<int>(static_cast<int64_t>(ks) * Kv / KS);
   const int ke = static_cast<int>(static_cast<int64_t>(ks + 1) * Kv / KS);
@@ -752,17 +753,43 @@ namespace moe {
 
 constexpr int kClipBlocks = 512;
 
+// Sum of squares of one array in float64.  Block b takes the b-th contiguous
+// range of its 8-element vectors (16-byte loads, four vectors in flight per
+// thread, four float64 accumulators per thread in a fixed assignment); the last
+// block also takes the n % 8 tail.  Deterministic: a fixed order throughout.
 template <typename T>
 __global__ __launch_bounds__(256) void clip_sumsq_kernel(const T* __restrict__ p, int64_t n,
                                                          double* __restrict__ part) {
+  constexpr int U = 4;
   __shared__ double red[256];
-  const int64_t b0 = n * blockIdx.x / gridDim.x, b1 = n * (blockIdx.x + 1) / gridDim.x;
-  double acc = 0.0;
-  for (int64_t i = b0 + threadIdx.x; i < b1; i += 256) {
-    const double v = static_cast<double>(ld_f32(p + i));
-    acc = fma(v, v, acc);
+  const int64_t n8 = n >> 3;
+  const int64_t b0 = n8 * blockIdx.x / gridDim.x, b1 = n8 * (blockIdx.x + 1) / gridDim.x;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += 256 * U) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = i + 256 * u;
+      if (j < b1) vec8<T>::load(p + 8 * j, v[u]);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double x = static_cast<double>(v[u][e]);
+        acc[e & 3] = fma(x, x, acc[e & 3]);
+      }
   }
-  red[threadIdx.x] = acc;
+  if (blockIdx.x == gridDim.x - 1)
+    for (int64_t i = 8 * n8 + threadIdx.x; i < n; i += 256) {
+      const double x = static_cast<double>(ld_f32(p + i));
+      acc[0] = fma(x, x, acc[0]);
+    }
+  red[threadIdx.x] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
@@ -796,13 +823,31 @@ __global__ __launch_bounds__(256) void clip_coef_kernel(const double* __restrict
   }
 }
 
+// p *= coef in place, 8-element vectors (two in flight per thread), the n % 8
+// tail by block 0.  coef == 1 leaves every value as it is (x * 1 rounds to x),
+// so the pass then reads and writes nothing.
 template <typename T>
 __global__ __launch_bounds__(256) void clip_scale_kernel(T* __restrict__ p, int64_t n,
                                                          const float* __restrict__ nc) {
+  constexpr int U = 2;
   const float c = nc[1];
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    st_f32(p + i, ld_f32(p + i) * c);
+  if (c == 1.0f) return;
+  const int64_t n8 = n >> 3, S = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8; i += S * U) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + u * S < n8) vec8<T>::load(p + 8 * (i + u * S), v[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + u * S < n8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[u][e] *= c;
+        vec8<T>::store(p + 8 * (i + u * S), v[u]);
+      }
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = 8 * n8 + threadIdx.x; i < n; i += 256) st_f32(p + i, ld_f32(p + i) * c);
 }
 
 template <typename T>

@@ -31,11 +31,7 @@ def _sample(ref, T, rng, n=40):
 
 
 # gated-linear-unit forms of two layer shapes (GELU gate: the GeGLU form)
-GLU_FULL = {
-    "switch_base_geglu_bf16": W.WORKLOADS["switch_base_bf16"].replace(name="switch_base_geglu_bf16",
-                                                                      act="gelu", glu=True),
-    "xmoe_top2_geglu_bf16": W.WORKLOADS["xmoe_top2_bf16"].replace(name="xmoe_top2_geglu_bf16", glu=True),
-}
+GLU_FULL = W.GLU_WORKLOADS
 
 
 @pytest.mark.parametrize("name", list(W.WORKLOADS) + list(GLU_FULL))

@@ -178,6 +178,14 @@ def test_sparse_clip(name):
             continue
         want = (before[key].float() * torch.tensor(c_gpu, dtype=torch.float32, device="cuda")).to(got[key].dtype)
         assert torch.equal(got[key], want), key
+    # clipping inactive (coef 1): the gradients keep their bits
+    clipped = {k: (None if v is None else v.clone()) for k, v in got.items()}
+    moe.sparse_clip(dev.cfg, got["dw_r"], got["dbias"], got["dw1"], got["dw2"], 1e30, nc, bws)
+    torch.cuda.synchronize()
+    assert float(nc.cpu()[1]) == 1.0
+    for key in ("dw_r", "dbias", "dw1", "dw2"):
+        if got[key] is not None:
+            assert torch.equal(got[key], clipped[key]), key
 
 
 @pytest.mark.parametrize("name", ["switch_small_bf16", "xmoe_small_bf16", "tiny_switch_f32"])
