@@ -5,9 +5,9 @@
 
 A step is one moe_forward call (router -> dispatch -> gather -> expert FFN ->
 combine) over the whole synthetic batch, inputs already resident in HBM.
-Prints ONE JSON line: tokens/s, the roofline of the dominant kernel (timed
-live with HIP events on the stream it runs on), and the CPU oracle timed on
-the host cores as a baseline.
+Prints ONE JSON line: tokens/s, the roofline of the dominant kernel (its
+duration inside the step, timed live with HIP events on the stream it runs on),
+and the CPU oracle timed on the host cores as a baseline.
 
 The default workload is the Switch-Base-shaped layer: T = 8192 tokens
 (8 sequences x 1024), d_model 768, d_ff 3072, 128 experts, top-1,
@@ -177,12 +177,35 @@ def main():
         return a.elapsed_time(b) * 1e3 / reps   # microseconds per call
 
     R = args.kernel_reps
-    kern_us = {
-        "router": timed(lambda: moe.router(cfg, x, w_r, bias, gid, idx2, gate2, ws, stream), R),
-        "dispatch": timed(lambda: moe.dispatch(cfg, x, idx_t, slot2, cnt2, st2, xe2, ws, stream), R),
+    # The forward's kernels inside the step: the step-wise calls in order (the kernels
+    # moe_forward launches, plus the dispatch call's own histogram pass), an event on the
+    # launch stream between consecutive calls, so each duration is the kernel in the
+    # context of the step (the previous kernel's output in flight, a cold weight stream).
+    hidden2, ye2 = torch.empty_like(hidden), torch.empty_like(y_e)
+    seq_names = ["router", "dispatch", "gemm_up", "gemm_down", "combine"]
+    seq_calls = [lambda: moe.router(cfg, x, w_r, bias, gid, idx2, gate2, ws, stream),
+                 lambda: moe.dispatch(cfg, x, idx2, slot2, cnt2, st2, xe2, ws, stream),
+                 lambda: moe.expert_up(cfg, xe2, cnt2, w1, hidden2, stream),
+                 lambda: moe.expert_down(cfg, hidden2, cnt2, w2, ye2, stream),
+                 lambda: moe.combine(cfg, ye2, idx2, slot2, gate2, y2, stream)]
+
+    def in_step(n):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq_calls) + 1)] for _ in range(n)]
+        for i in range(n):
+            evs[i][0].record(stream)
+            for j, call in enumerate(seq_calls):
+                call()
+                evs[i][j + 1].record(stream)
+        torch.cuda.synchronize()
+        return {nm: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(n)) * 1e3 / n
+                for j, nm in enumerate(seq_names)}
+
+    in_step(2)
+    kern_us = in_step(args.steps)
+    # the same launches repeated alone (back to back, warm caches): for reference
+    isolated_us = {
         "gemm_up": timed(lambda: moe.expert_up(cfg, x_e, cnt_t, w1, hidden, stream), R),
         "gemm_down": timed(lambda: moe.expert_down(cfg, hidden, cnt_t, w2, y_e, stream), R),
-        "combine": timed(lambda: moe.combine(cfg, y_e, idx_t, slot_t, gate_t, y2, stream), R),
     }
     if wl.route == "topk":  # router + load-balancing loss (Eq. 4-6)
         aux_t = torch.empty(1 + 2 * wl.E, dtype=torch.float32, device=dev)
@@ -299,6 +322,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "isolated_us": {n: round(v, 2) for n, v in isolated_us.items()},
         "grouped_gemm_mfma_frac": round((algo["gemm_up"]["flops"] + algo["gemm_down"]["flops"]) /
                                         ((kern_us["gemm_up"] + kern_us["gemm_down"]) / 1e6) /
                                         (peak_flops * 1e12), 4),

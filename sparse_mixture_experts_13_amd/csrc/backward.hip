@@ -285,13 +285,23 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
     }
   };
   // fragment of operand rows r (32 rows starting at r0), k = 16 j + 8 half .. + 7
-  auto frag = [&](const bf16_t* t, bool kc, int pitch, int r, int j) {
+  // Fragment of operand rows r0 .. r0 + 31 (lane row r0 + fr), k = 16 j + 8 half .. + 7.
+  // A [row][k] tile is read as one 16-byte vector.  A [k][row] tile is read with two
+  // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the
+  // 8-byte chunks addressed by lanes 4 q + i / 4 (q = 0..3), so lane 16 g + 4 q + c
+  // addresses row chunk r0 + 16 (g % 2) + 4 c of k row 8 (g / 2) + q (+ 4 for the
+  // second read) and every lane ends with 4 + 4 consecutive k of its own row.
+  const int trq = (lane & 15) >> 2, trc = lane & 3, trg = lane >> 4;
+  auto frag = [&](const bf16_t* t, bool kc, int pitch, int r0, int j) {
     const int k = 16 * j + 8 * half;
-    if (kc) return *reinterpret_cast<const bf16x8*>(t + r * pitch + k);
-    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
-    u16x8 v;  // raw bits: a bf16 vector element would convert the integer's value
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = t[(k + i) * pitch + r];
+    if (kc) return *reinterpret_cast<const bf16x8*>(t + (r0 + fr) * pitch + k);
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const bf16_t* src = t + (16 * j + 8 * (trg >> 1) + trq) * pitch + r0 + 16 * (trg & 1) + 4 * trc;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(src + 4 * pitch));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
   };
 
@@ -315,9 +325,9 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
       for (int j = 0; j < BK / 16; ++j) {
         bf16x8 fa[TM], fb[TN];
 #pragma unroll
-        for (int t = 0; t < TM; ++t) fa[t] = frag(la[buf], AKC, TA::kPitch, (wm * TM + t) * 32 + fr, j);
+        for (int t = 0; t < TM; ++t) fa[t] = frag(la[buf], AKC, TA::kPitch, (wm * TM + t) * 32, j);
 #pragma unroll
-        for (int i = 0; i < TN; ++i) fb[i] = frag(lb[buf], BKC, TBt::kPitch, (wn * TN + i) * 32 + fr, j);
+        for (int i = 0; i < TN; ++i) fb[i] = frag(lb[buf], BKC, TBt::kPitch, (wn * TN + i) * 32, j);
 #pragma unroll
         for (int i = 0; i < TN; ++i)
 #pragma unroll
