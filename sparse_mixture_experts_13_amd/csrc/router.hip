@@ -140,21 +140,40 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
                                                            int Epad, int d,
                                                            bf16_t* __restrict__ planes,
                                                            int* __restrict__ flags) {
+  // eight elements per thread and step (d is a multiple of 64, so E * d and
+  // Epad * d are multiples of 8): 16-byte loads, three 16-byte plane stores
   const int64_t n = static_cast<int64_t>(Epad) * d;
   const int64_t lim = static_cast<int64_t>(E) * d;
   int nz = 0;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const float w = i < lim ? w_r[i] : 0.f;
-    const bf16_t hi = f32_to_bf16(w);
-    const float r1 = w - bf16_to_f32(hi);
-    const bf16_t mid = f32_to_bf16(r1);
-    const float r2 = r1 - bf16_to_f32(mid);
-    const bf16_t lo = f32_to_bf16(r2);
-    planes[i] = hi;
-    planes[n + i] = mid;
-    planes[2 * n + i] = lo;
-    nz |= ((mid & 0x7FFF) | (lo & 0x7FFF)) != 0;
+  for (int64_t i8 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i8 < n / 8;
+       i8 += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t i = i8 * 8;
+    float w[8];
+    vec8<float>::load(w_r + (i < lim ? i : 0), w);
+    u32x4 ph, pm, pl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float wj = i < lim ? w[j] : 0.f;
+      const bf16_t hi = f32_to_bf16(wj);
+      const float r1 = wj - bf16_to_f32(hi);
+      const bf16_t mid = f32_to_bf16(r1);
+      const float r2 = r1 - bf16_to_f32(mid);
+      const bf16_t lo = f32_to_bf16(r2);
+      const int sh = 16 * (j & 1);
+      if (sh == 0) {
+        ph[j >> 1] = hi;
+        pm[j >> 1] = mid;
+        pl[j >> 1] = lo;
+      } else {
+        ph[j >> 1] |= static_cast<uint32_t>(hi) << 16;
+        pm[j >> 1] |= static_cast<uint32_t>(mid) << 16;
+        pl[j >> 1] |= static_cast<uint32_t>(lo) << 16;
+      }
+      nz |= ((mid & 0x7FFF) | (lo & 0x7FFF)) != 0;
+    }
+    *reinterpret_cast<u32x4*>(planes + i) = ph;
+    *reinterpret_cast<u32x4*>(planes + n + i) = pm;
+    *reinterpret_cast<u32x4*>(planes + 2 * n + i) = pl;
   }
   nz = __syncthreads_or(nz);
   if (threadIdx.x == 0) flags[blockIdx.x] = nz;
@@ -286,12 +305,34 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   int* hl = reinterpret_cast<int*>(smem + body);  // [k][Epad]
   for (int i = tid; i < k * Epad; i += 256) hl[i] = 0;
 
-  int any = 0;
-  for (int i = 0; i < kSplitBlocks; ++i) any |= flags[i];
+  // the split kernel's flags, one per lane in a single vector load, then a wave
+  // vote (one memory latency)
+  static_assert(kSplitBlocks == kWave, "one split flag per lane");
+  const int any = __any(flags[lane] != 0) ? 1 : 0;
   const int KS = d / 64;
   const int total = (any ? 3 : 1) * KS;
   const int64_t plane_elems = static_cast<int64_t>(Epad) * d;
 
+  // Loads of one stage: this wave's instructions q (rows (4 q + wave) * 8 .. + 7,
+  // lane row row_q = ... + lane / 8) for q < R; RMAX bounds R at compile time so the
+  // issue loop unrolls, and each lane's row offsets are computed once: a stage only
+  // adds its k offset (and the plane offset).
+  constexpr int RMAX = 4 * EW + TT;
+  int64_t roff[RMAX];  // element offset of this lane's 16-byte chunk at k = 0
+  bool rw[RMAX];       // weight row (else token row)
+#pragma unroll
+  for (int q = 0; q < RMAX; ++q) {
+    const int rbase = (q * 4 + wave) * 8;
+    const int row = rbase + (lane >> 3);
+    const int c = (lane & 7) ^ lds_swz(row);
+    rw[q] = rbase < Epad;
+    if (rw[q]) roff[q] = static_cast<int64_t>(row) * d + c * 8;
+    else roff[q] = static_cast<int64_t>(min(tok0 + row - Epad, T - 1)) * d + c * 8;
+  }
+  // (the lambda below reads the arrays through pointers: capturing an array whose
+  // size depends on the template arguments leaves the kernel uninstantiated on the host)
+  const int64_t* roffp = roff;
+  const bool* rwp = rw;
   // Blocks start their k loop at different offsets so that they do not all
   // read the same router-weight rows at the same moment (hot L2 channels).
   const int rot = b % KS;
@@ -299,21 +340,13 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     const int p = st / KS;
     int ks = st - p * KS + rot;
     ks = ks >= KS ? ks - KS : ks;
-    const bf16_t* wp = planes + p * plane_elems;
-    unsigned char* base = smem + slot * STAGE;
-    for (int q = 0; q < R; ++q) {
-      const int rbase = (q * 4 + wave) * 8;  // first of the 8 rows this wave loads
-      const int row = rbase + (lane >> 3);
-      const int c = (lane & 7) ^ lds_swz(row);
-      const bf16_t* src;
-      if (rbase < Epad) {
-        src = wp + static_cast<int64_t>(row) * d + ks * 64 + c * 8;
-      } else {
-        const int t = min(tok0 + row - Epad, T - 1);
-        src = x + static_cast<int64_t>(t) * d + ks * 64 + c * 8;
-      }
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + (q * 4 + wave) * 1024), 16, 0, 0);
-    }
+    const bf16_t* wp = planes + p * plane_elems + ks * 64;
+    const bf16_t* xp = x + ks * 64;
+    unsigned char* base = smem + slot * STAGE + wave * 1024;
+#pragma unroll
+    for (int q = 0; q < RMAX; ++q)
+      if (q < R)
+        __builtin_amdgcn_global_load_lds((rwp[q] ? wp : xp) + roffp[q], (lds_void*)(base + q * 4096), 16, 0, 0);
   };
 
   floatx16 acc[EW][TT];
@@ -332,27 +365,31 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     ring_barrier();
     if (st + S - 1 < total) issue(st + S - 1, (st + S - 1) % S);
     const unsigned char* sb = smem + (st % S) * STAGE;
+    // every fragment of the stage first (one LDS latency), then the MFMAs
+    bf16x8 bq[4][TT], a[4][EW];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = 2 * j + half;
-      bf16x8 bq[TT];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         const int row = Epad + tt * 32 + fr;
-        bq[tt] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
+        bq[j][tt] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
       }
 #pragma unroll
       for (int u = 0; u < EW; ++u) {
-        const int et = wave + 4 * u;
-        if (et < n_et) {
-          const int row = et * 32 + fr;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-            acc[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[tt], acc[u][tt], 0, 0, 0);
-        }
+        const int row = min(wave + 4 * u, n_et - 1) * 32 + fr;
+        a[j][u] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
       }
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int u = 0; u < EW; ++u)
+        if (wave + 4 * u < n_et) {
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+            acc[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][u], bq[j][tt], acc[u][tt], 0, 0, 0);
+        }
   }
   __syncthreads();  // ring reads done before the logits tile overwrites it
 
