@@ -246,8 +246,9 @@ int64_t moe_backward_workspace_bytes(const moe_config* cfg);
  *   bws   workspace of moe_backward_workspace_bytes(cfg) bytes.
  * bf16: products on bf16 MFMA with float32 accumulation; dy_e = gate * dy, dZ,
  * dx_e and the outputs are rounded to bf16; the pre-activation (GELU, and both
- * halves for GLU) is recomputed in bf16.  The router gradient is float32; its token contraction is
- * split into 64 ranges added in order, so repeated calls give identical bits. */
+ * halves for GLU) is recomputed in bf16.  The router gradient is float32 (float32 MFMA); its token
+ * contraction is split into at most 64 ranges (a function of E and d_model)
+ * added in order, so repeated calls give identical bits. */
 int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
                  const void* w1, const void* w2, const void* dy, void* dx, float* dw_r,
                  float* dbias, void* dw1, void* dw2, void* ws, void* bws, void* stream);

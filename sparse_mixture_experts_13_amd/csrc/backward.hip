@@ -24,20 +24,23 @@
 // row-contiguous (the weights in dH = dy_e . w2 and dx_e = dZ . w1, and both
 // token-major operands of the weight gradients, whose contraction runs over
 // the tokens of an expert) is staged as [k][row] with 16-byte stores and read
-// as eight 2-byte values per fragment.  Register-staged double buffering,
-// 64-k steps (32 for the token-contracted ones), v_mfma_f32_32x32x16_bf16 with float32 accumulation, D = B . A^T
+// with two LDS transpose reads (ds_read_b64_tr_b16) per fragment.
+// Register-staged double buffering, 64-k steps (32 for the token-contracted
+// ones), v_mfma_f32_32x32x16_bf16 with float32 accumulation, D = B . A^T
 // so each lane stores four consecutive output columns.  act' is applied in the
 // dH epilogue (from the hidden activation for ReLU, from the recomputed
 // pre-activation for GELU).  The router products (K = E or K = T) and the
-// float32 layers use a float32 FMA tile kernel with the same orientation
-// flags; the token-contracted router weight gradient is split over 64 token
-// ranges and the ranges are added in order (deterministic, no atomics).
+// float32 layers use a float32 MFMA tile kernel (v_mfma_f32_32x32x2_f32) with
+// the same orientation flags; the token-contracted router weight gradient is
+// split over up to 64 token ranges and the ranges are added in order
+// (deterministic, no atomics).
 #include "moe_common.h"
 #include "moe_internal.h"
 
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace moe {
 
@@ -413,8 +416,8 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// float32 FMA tile GEMM with the same orientation flags, 64 x 64 tile, BK 16,
-// 4 x 4 outputs per thread.  Inputs of type TA / TB (float or bf16), float32
+// float32 MFMA tile GEMM with the same orientation flags, 64 x 64 tile of four
+// 32 x 32 wave tiles.  Inputs of type TA / TB (float or bf16), float32
 // accumulation, output float32 or TO.  Batched over z = e * KS + ks: KS > 1
 // splits the k range into KS contiguous pieces, piece ks going to output slice
 // ks (out + ks * sOk), added later in order.  Per expert e: M_e / K_e as in
@@ -432,8 +435,14 @@ __global__ __launch_bounds__(256) void fgemm_kernel(
     const TA* __restrict__ A, int64_t sAe, int lda, const TB* __restrict__ B, int64_t sBe, int ldb,
     TO* __restrict__ out, int64_t sOe, int64_t sOk, int ldo, const TO* __restrict__ aux,
     const int32_t* __restrict__ count, int64_t C, int M, int N, int K, bool m_is_count, int KS) {
-  __shared__ float sa[16][65];
-  __shared__ float sb[16][65];
+  // 32-k steps through double-buffered LDS tiles [k][row] (the next step's
+  // elements loaded into registers while this step's MFMAs run); wave (wm, wn)
+  // owns the 32 x 32 sub-tile; v_mfma_f32_32x32x2_f32 with srcA = rows n of B
+  // and srcB = rows m of A gives D[n][m], lane l holding m = l % 32 and
+  // n = 8 (r / 4) + 4 (l / 32) + r % 4 of accumulator element r.
+  constexpr int FBK = 32, P = 64 + 4, PL = FBK * 64 / 256;
+  __shared__ float sa[2][FBK][P];
+  __shared__ float sb[2][FBK][P];
   const int bx = blockIdx.x, by = blockIdx.y;
   const int e = blockIdx.z / KS, ks = blockIdx.z % KS;
   int Mv = M, Kv = K;
@@ -449,53 +458,93 @@ __global__ __launch_bounds__(256) void fgemm_kernel(
   const int ke = static_cast<int>(static_cast<int64_t>(ks + 1) * Kv / KS);
   const TA* Ae = A + e * sAe;
   const TB* Be = B + e * sBe;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-  float acc[4][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, fr = lane & 31, kh = lane >> 5;
+  // tile element q of a step: (row r in 0..63, k c in 0..FBK-1); which index runs
+  // fastest follows the storage so that neighbouring threads read neighbouring memory
+  // A row-contiguous operand ([k][row] storage) is read as 8 consecutive rows of
+  // one k per thread (one 16-byte load of bf16, two of float; element loads for a
+  // chunk that crosses the row extent or sits at an unaligned pitch); a
+  // k-contiguous one element by element, k fastest.
+  static_assert(PL == 8, "one 8-row chunk of one k per thread");
+  float va[PL], vb[PL];
+  auto fetch_op = [&](auto* P0, int ld, int r0, int ext, bool kc, int k0, float* v) {
+    if (kc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < PL; ++i) {
+        const int q = tid + 256 * i;
+        const int r = r0 + q / FBK, kk = k0 + q % FBK;
+        v[i] = (r < ext && kk < ke) ? ld_f32(P0 + static_cast<int64_t>(r) * ld + kk) : 0.f;
+      }
+    } else {
+      const int kk = k0 + (tid >> 3), rb = r0 + (tid & 7) * 8;
+      const auto* src = P0 + static_cast<int64_t>(kk) * ld + rb;
+      if (kk < ke && rb + 8 <= ext && (ld & 7) == 0) {
+        vec8<typename std::remove_const<typename std::remove_pointer<decltype(P0)>::type>::type>::load(src, v);
+      } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int k0 = kb; k0 < ke; k0 += 16) {
+        for (int j = 0; j < 8; ++j) v[j] = (kk < ke && rb + j < ext) ? ld_f32(src + j) : 0.f;
+      }
+    }
+  };
+  auto fetch = [&](int k0) {
+    fetch_op(Ae, lda, m0, M, AKC, k0, va);
+    fetch_op(Be, ldb, n0, N, BKC, k0, vb);
+  };
+  auto put = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < PL; ++i) {
       const int q = tid + 256 * i;
-      // tile element (row r in 0..63, k c in 0..15); which index runs fastest
-      // follows the storage so that neighbouring threads read neighbouring memory
-      const int r = AKC ? q >> 4 : q & 63, c = AKC ? q & 15 : q >> 6;
-      const int m = m0 + r, kk = k0 + c;
-      sa[c][r] = (m < M && kk < ke) ? ld_f32(Ae + (AKC ? static_cast<int64_t>(m) * lda + kk
-                                                       : static_cast<int64_t>(kk) * lda + m)) : 0.f;
-      const int r2 = BKC ? q >> 4 : q & 63, c2 = BKC ? q & 15 : q >> 6;
-      const int n = n0 + r2, kk2 = k0 + c2;
-      sb[c2][r2] = (n < N && kk2 < ke) ? ld_f32(Be + (BKC ? static_cast<int64_t>(n) * ldb + kk2
-                                                          : static_cast<int64_t>(kk2) * ldb + n)) : 0.f;
+      if constexpr (AKC) sa[buf][q % FBK][q / FBK] = va[i];
+      else sa[buf][tid >> 3][(tid & 7) * 8 + i] = va[i];
+      if constexpr (BKC) sb[buf][q % FBK][q / FBK] = vb[i];
+      else sb[buf][tid >> 3][(tid & 7) * 8 + i] = vb[i];
     }
+  };
+  floatx16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  if (kb < ke) {
+    fetch(kb);
+    put(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = kb; k0 < ke; k0 += FBK) {
+    const bool more = k0 + FBK < ke;
+    if (more) fetch(k0 + FBK);
+#pragma unroll
+    for (int kk = 0; kk < FBK / 2; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sb[buf][2 * kk + kh][wn * 32 + fr],
+                                                 sa[buf][2 * kk + kh][wm * 32 + fr], acc, 0, 0, 0);
+    if (more) put(buf ^ 1);
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sa[kk][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = sb[kk][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
+    buf ^= 1;
   }
   TO* Oe = out + e * sOe + ks * sOk;
   const TO* Ze = aux ? aux + e * sOe : nullptr;
+  const int m = m0 + wm * 32 + fr;
+  if (m < Mv) {
+    if constexpr (EPI == 0 && sizeof(TO) == 4) {
+      if ((ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(Oe) & 15) == 0) {
+        // four consecutive columns per lane and group: one 16-byte store
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty + 16 * i;
-    if (m >= Mv) continue;
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * 32 + 8 * q + 4 * kh;
+          if (n + 3 < N)
+            *reinterpret_cast<floatx4*>(Oe + static_cast<int64_t>(m) * ldo + n) =
+                floatx4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+          else
+            for (int u = 0; u < 4 && n + u < N; ++u) st_f32(Oe + static_cast<int64_t>(m) * ldo + n + u, acc[4 * q + u]);
+        }
+        return;
+      }
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx + 16 * j;
+    for (int r = 0; r < 16; ++r) {
+      const int n = n0 + wn * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
       if (n >= N) continue;
-      float v = acc[i][j];
+      float v = acc[r];
       if constexpr (EPI == 1) {
         const float z = ld_f32(Ze + static_cast<int64_t>(m) * ldo + n);
         v *= ACT == 0 ? (z > 0.f ? 1.f : 0.f) : gelu_grad(z);
@@ -716,13 +765,17 @@ static hipError_t backward_typed(const Plan& p, const BwdArgs& a, hipStream_t s)
     MOE_TRY((run_fgemm<float, float, float, true, false, 0, 0>(1, 0, a.dh, 0, p.Epad, a.w_r, 0, d, dx_r, 0,
                                                                 0, d, nullptr, nullptr, T_, d, p.E, false, 1,
                                                                 s)));
-    // dw_r[e][d] = sum_t dh[t][e] x[t][d], in kBwdSplit token ranges added in order
+    // dw_r[e][d] = sum_t dh[t][e] x[t][d], in KS token ranges added in order; KS, a
+    // function of the sizes only, gives about 384 tiles (16 on Switch-Base), at
+    // most kBwdSplit
     const int64_t n = int64_t(p.E) * d;
+    const int64_t tiles = int64_t((d + 63) / 64) * ((p.E + 63) / 64);
+    const int KS = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kBwdSplit, (384 + tiles - 1) / tiles)));
     MOE_TRY((run_fgemm<float, T, float, false, false, 0, 0>(1, 0, a.dh, 0, p.Epad, static_cast<const T*>(a.x),
                                                              0, d, a.dwr_part, 0, n, d, nullptr, nullptr,
-                                                             p.E, d, T_, false, kBwdSplit, s)));
+                                                             p.E, d, T_, false, KS, s)));
     hipLaunchKernelGGL(sum_slices_kernel, dim3(static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 1024))),
-                       dim3(256), 0, s, a.dwr_part, n, kBwdSplit, a.dw_r);
+                       dim3(256), 0, s, a.dwr_part, n, KS, a.dw_r);
     MOE_TRY(hipGetLastError());
     if (a.dbias) {
       hipLaunchKernelGGL(bwd_bias_kernel, dim3((p.E + 63) / 64), dim3(64), 0, s, a.dh, p.Epad, T_, p.E,
