@@ -634,6 +634,21 @@ static hipError_t run_fgemm(int batch, int64_t C, const TA* A, int64_t sAe, int 
     if (err_ != hipSuccess) return err_;   \
   } while (0)
 
+// Token-row products (dZ, dx_e): 64-row tiles while one tile holds an expert's
+// tokens (capacity <= 64: weight streaming), 128-row tiles above (MFMA-bound;
+// 4% faster on the large layer's backward).
+template <int EPI, int ACT>
+static hipError_t run_bgemm_rows(const Plan& p, const bf16_t* A, int64_t sAe, int lda, const bf16_t* B,
+                                 int64_t sBe, int ldb, bf16_t* out, int64_t sOe, int ldo,
+                                 const bf16_t* aux, const int32_t* count, int M, int N, int K,
+                                 bool m_is_count, hipStream_t s) {
+  if (p.C > 64)
+    return run_bgemm<128, 128, 64, true, false, EPI, ACT>(p, A, sAe, lda, B, sBe, ldb, out, sOe, ldo, aux,
+                                                           count, M, N, K, m_is_count, s);
+  return run_bgemm<64, 128, 64, true, false, EPI, ACT>(p, A, sAe, lda, B, sBe, ldb, out, sOe, ldo, aux, count,
+                                                        M, N, K, m_is_count, s);
+}
+
 // Expert-side products for one dtype.  dZ is staged in the dZ buffer, the
 // pre-activation (GELU) in the Z buffer.  GLU: Z = x_e [W; V]^T over the 2 f
 // stacked rows in the Z buffer ([C][2 f] per expert), dZ = (dZa, dZb) likewise,
@@ -667,20 +682,20 @@ hipError_t expert_backward<bf16_t>(const Plan& p, const bf16_t* x_e, const bf16_
   // dZ[s][f] = sum_d dy_e[s][d] w2[d][f] * act'(Z)   (A = dy_e k-contiguous, B = w2 [k=d][n=f])
   if (p.glu) {
     if (p.act == 0)
-      MOE_TRY((run_bgemm<64, 128, 64, true, false, 2, 0>(p, dy_e, sX, d, w2, sW, f, dz, sZ, r, z, count, Ci,
+      MOE_TRY((run_bgemm_rows<2, 0>(p, dy_e, sX, d, w2, sW, f, dz, sZ, r, z, count, Ci,
                                                       f, d, true, s)));
     else
-      MOE_TRY((run_bgemm<64, 128, 64, true, false, 2, 1>(p, dy_e, sX, d, w2, sW, f, dz, sZ, r, z, count, Ci,
+      MOE_TRY((run_bgemm_rows<2, 1>(p, dy_e, sX, d, w2, sW, f, dz, sZ, r, z, count, Ci,
                                                       f, d, true, s)));
   } else if (p.act == 0) {
-    MOE_TRY((run_bgemm<64, 128, 64, true, false, 1, 0>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
+    MOE_TRY((run_bgemm_rows<1, 0>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
                                                     f, d, true, s)));
   } else {
-    MOE_TRY((run_bgemm<64, 128, 64, true, false, 1, 1>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
+    MOE_TRY((run_bgemm_rows<1, 1>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
                                                     f, d, true, s)));
   }
   // dx_e[s][d] = sum_r dZ[s][r] w1[r][d]   (B = w1 [k=r][n=d])
-  MOE_TRY((run_bgemm<64, 128, 64, true, false, 0, 0>(p, dz, sZ, r, w1, sW1, d, dx_e, sX, d, nullptr, count,
+  MOE_TRY((run_bgemm_rows<0, 0>(p, dz, sZ, r, w1, sW1, d, dx_e, sX, d, nullptr, count,
                                                   Ci, d, r, true, s)));
   // dw2[d][f] = sum_s dy_e[s][d] H[s][f]   (A = dy_e [k=s][m=d], B = H [k=s][n=f])
   MOE_TRY((run_bgemm<128, 128, 32, false, false, 0, 0>(p, dy_e, sX, d, hidden, sH, f, dw2, sW, f, nullptr,
