@@ -280,7 +280,10 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
   const int total = (v1 - v0) * KS;
   if (total == 0) return;
 
-  // a tile cursor: expert, row block, column block of linear non-empty tile v
+  // a tile cursor: expert, row block, column block of linear non-empty tile v;
+  // with temporal weights (row blocks re-read the weight tiles) the row blocks
+  // of a weight tile are consecutive, so its re-reads hit L2 (X-MoE top-2: 3-4%
+  // faster than column blocks fastest)
   struct Cur { int v, e, mb, nb, cnt; };
   auto seek = [&](Cur& c, int v) {
     c.v = v;
@@ -288,13 +291,28 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
     while (pre[e + 1] <= v) ++e;
     const int local = v - pre[e];
     c.e = e;
-    c.mb = local / n_nb;
-    c.nb = local - c.mb * n_nb;
     c.cnt = rows_of(e);
+    if constexpr (!NTW) {
+      const int nmb = (c.cnt + BM - 1) / BM;
+      c.nb = local / nmb;
+      c.mb = local - c.nb * nmb;
+    } else {
+      c.mb = local / n_nb;
+      c.nb = local - c.mb * n_nb;
+    }
   };
   auto next = [&](Cur& c) {
     ++c.v;
-    if (++c.nb == n_nb) {
+    if constexpr (!NTW) {
+      if (++c.mb == (c.cnt + BM - 1) / BM) {
+        c.mb = 0;
+        ++c.nb;
+        if (c.v < pre[c.e + 1]) return;
+        do { ++c.e; } while (c.e < E && pre[c.e + 1] <= c.v);
+        c.nb = 0;
+        if (c.e < E) c.cnt = rows_of(c.e);
+      }
+    } else if (++c.nb == n_nb) {
       c.nb = 0;
       ++c.mb;
       if (c.v < pre[c.e + 1]) return;
