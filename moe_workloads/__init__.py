@@ -127,6 +127,13 @@ TEST_WORKLOADS = {
                                 capacity_factor=1.0, act="relu", dtype="bf16", glu=True),
     "reglu_small_f32": Workload("reglu_small_f32", T=600, d_model=128, d_ff=192, E=8, k=1,
                                 capacity_factor=1.25, act="relu", dtype="f32", glu=True),
+    # capacity > 384 with a contraction of 2048: the down-projection (K = d_ff) of a
+    # top-2 GELU layer with 128 output columns (half a 256-row weight tile), and the
+    # GeGLU up-projection (K = d_model) with two 256-row blocks per expert
+    "longk_top2_bf16": Workload("longk_top2_bf16", T=900, d_model=128, d_ff=2048, E=4, k=2,
+                                capacity_factor=1.0, act="gelu", dtype="bf16"),
+    "geglu_longk_bf16": Workload("geglu_longk_bf16", T=900, d_model=2048, d_ff=192, E=3, k=1,
+                                 capacity_factor=1.6, act="gelu", dtype="bf16", glu=True),
 }
 
 

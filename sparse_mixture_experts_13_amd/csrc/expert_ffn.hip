@@ -306,7 +306,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
   struct Cur { int v, e, mb, nb, cnt; };
   auto seek = [&](Cur& c, int v) {
     c.v = v;
-    int e = 0;
+    int e = c.e;  // tiles are visited in increasing order: resume the search
     while (pre[e + 1] <= v) ++e;
     const int local = v - pre[e];
     c.e = e;
@@ -353,6 +353,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
   };
 
   Cur lc, cc;
+  lc.e = 0;
   seek(lc, v0);
   cc = lc;
   int lk = 0;
@@ -500,6 +501,258 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
     }
     step(cc);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong grouped GEMM for large capacities, where a tile re-reads its weight
+// rows for several row blocks and the MFMA pipe, not HBM, sets the pace.
+//
+// Block tile: 256 activation rows x 256 weight rows, persistent blocks of 8
+// waves in two groups of four (waves w and w + 4 share a SIMD).  Wave (g, wn)
+// owns activation rows 128 g .. 128 g + 127 and weight rows 64 wn .. 64 wn + 63
+// of the tile: 4 x 2 MFMA tiles of 32 x 32.  The k loop runs in 32-k stages
+// through a 4-slot direct-to-LDS ring (32 KB a stage), and every stage has two
+// phases separated by block barriers:
+//   * memory phase: read the wave's 12 fragments of the stage from LDS, issue
+//     its 4 direct-to-LDS loads of the stage three ahead, wait for its own
+//     loads of the next stage;
+//   * MFMA phase: 16 MFMAs on the fragments in registers (and the tile's
+//     epilogue after its last stage).
+// Group 1 runs one phase behind group 0, so on every SIMD one wave issues
+// MFMAs while the other feeds LDS and memory: the matrix pipe never waits for
+// a fragment read or a barrier of its own wave.  A stage's loads are issued
+// three stages before its first reader and waited for one stage before, so
+// about 64 KB per CU are in flight.  Tiles (expert, row block, column block),
+// the per-XCD strided share of them and the clamped rows past the count are as
+// in the ring kernel above; the loads of the block's last stages re-read its
+// final stage into free slots, so every memory phase issues the same loads and
+// waits on one fixed memory-counter threshold.
+// ---------------------------------------------------------------------------
+constexpr int kPpBM = 256, kPpBN = 256, kPpBK = 32, kPpSlots = 4;
+
+__host__ __device__ constexpr int ffn_pp_lds_bytes() {
+  return kPpSlots * (kPpBM + kPpBN) * kPpBK * 2 + (2 * kMaxE + 1) * 4;
+}
+
+template <int ACT, bool GLU>
+__global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
+    const int32_t* __restrict__ count, int E, int64_t C, int N, int K) {
+  constexpr int BM = kPpBM, BN = kPpBN, BK = kPpBK, R = kPpSlots;
+  constexpr int TM = 4, TN = 2;          // MFMA tiles per wave (activation, weight)
+  constexpr int RB = BK * 2;             // LDS row bytes
+  constexpr int CPR = BK / 8;            // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;         // rows per wave instruction
+  constexpr int WL = BN / RPI / 8;       // weight instructions per wave per stage
+  constexpr int AL = BM / RPI / 8;       // activation instructions per wave per stage
+  constexpr int PER = WL + AL;
+  constexpr int STAGE = (BN + BM) * RB;
+  static_assert(BM == 2 * TM * 32 && BN == 4 * TN * 32, "wave grid");
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* pre = reinterpret_cast<int*>(smem + R * STAGE);  // [E + 1] tile prefix per expert
+  int* cnts = pre + kMaxE + 1;                            // [E] clamped row counts
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wn = wave & 3;
+  const int half = lane >> 5, fr = lane & 31;
+  const int n_nb = (N + BN - 1) / BN;
+  const int KS = K / BK;
+
+  auto rows_of = [&](int e) {
+    int64_t c = count[e];
+    return static_cast<int>(c < 0 ? 0 : (c > C ? C : c));
+  };
+  if (wave == 0) {
+    int run = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+      const int e = e0 + lane;
+      const int r = e < E ? rows_of(e) : 0;
+      const int t = (r + BM - 1) / BM * n_nb;
+      const int incl = wave_inclusive_scan(t, lane) + run;
+      if (e < E) {
+        pre[e + 1] = incl;
+        cnts[e] = r;
+      }
+      run = __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane == 0) pre[0] = 0;
+  }
+  __syncthreads();
+  const int V = pre[E];
+  const int G = gridDim.x;
+  // each XCD takes a contiguous eighth of the tiles, its blocks take them strided
+  const int NX = G < 8 ? G : 8;
+  const int xg = blockIdx.x % NX, jb = blockIdx.x / NX;
+  const int v0 = static_cast<int>(static_cast<int64_t>(xg) * V / NX) + jb;
+  const int v1 = static_cast<int>(static_cast<int64_t>(xg + 1) * V / NX);
+  const int vs = (G - xg + NX - 1) / NX;
+  const int ntile = v0 < v1 ? (v1 - v0 + vs - 1) / vs : 0;
+  const int total = ntile * KS;
+  if (total == 0) return;
+
+  // tile cursor; the row blocks of a weight tile are consecutive.  A block visits
+  // its tiles in increasing order, so the expert search resumes where the
+  // previous tile's expert was (E + tiles steps over the whole launch).
+  struct Cur { int v, e, mb, nb, cnt; };
+  auto seek = [&](int v, int e) {
+    Cur c;
+    c.v = v;
+    while (pre[e + 1] <= v) ++e;
+    const int local = v - pre[e];
+    c.e = e;
+    c.cnt = cnts[e];
+    const int nmb = (c.cnt + BM - 1) / BM;
+    c.nb = local / nmb;
+    c.mb = local - c.nb * nmb;
+    return c;
+  };
+  // the next tile of this block; past its last tile the cursor is never used
+  // for an address, and seek must not scan past pre[E]
+  auto step = [&](Cur c) { return c.v + vs < V ? seek(c.v + vs, c.e) : c; };
+
+  Cur lc = seek(v0, 0), cc = lc;
+  int lk = 0;
+  auto issue_stage = [&](int slot) {
+    unsigned char* base = smem + slot * STAGE;
+    const bf16_t* We = W + static_cast<int64_t>(lc.e) * N * K;
+    const bf16_t* Ae = A + static_cast<int64_t>(lc.e) * C * K;
+#pragma unroll
+    for (int q = 0; q < WL; ++q) {
+      const int p = (wave * WL + q) * 64 + lane;
+      const int row = p / CPR;
+      const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
+      int wr = min(lc.nb * BN + row, N - 1);
+      if constexpr (GLU) wr = glu_row(wr, N >> 1);
+      const uint32_t off = static_cast<uint32_t>(wr) * K + lk * BK + c * 8;
+      __builtin_amdgcn_global_load_lds(We + off, (lds_void*)(base + (wave * WL + q) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < AL; ++q) {
+      const int p = (wave * AL + q) * 64 + lane;
+      const int row = p / CPR;
+      const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
+      const uint32_t off = static_cast<uint32_t>(min(lc.mb * BM + row, lc.cnt - 1)) * K + lk * BK + c * 8;
+      __builtin_amdgcn_global_load_lds(Ae + off, (lds_void*)(base + BN * RB + (wave * AL + q) * 1024),
+                                       16, 0, 0);
+    }
+  };
+  // the loader cursor stops on the block's last stage: later issues re-read it
+  auto advance = [&]() {
+    if (++lk == KS) {
+      lk = 0;
+      lc = step(lc);
+    }
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    ring_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  floatx16 acc[TN][TM];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
+  };
+
+#pragma unroll
+  for (int x = 0; x < R - 1; ++x) {
+    issue_stage(x);
+    if (x + 1 < total) advance();
+  }
+  wait_vmcnt<(R - 2) * PER>();  // this wave's loads of stage 0
+  barrier();
+  if (grp == 1) barrier();  // group 1 runs one phase behind
+  zero_acc();
+  int kk = 0;
+  for (int s = 0; s < total; ++s) {
+    // memory phase
+    const unsigned char* sw = smem + (s % R) * STAGE;
+    const unsigned char* sa = sw + BN * RB;
+    bf16x8 fa[2][TN], fb[2][TM];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = 2 * j + half;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int row = (grp * TM + t) * 32 + fr;
+        fb[j][t] = *reinterpret_cast<const bf16x8*>(sa + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int row = (wn * TN + i) * 32 + fr;
+        fa[j][i] = *reinterpret_cast<const bf16x8*>(sw + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
+      }
+    }
+    issue_stage((s + R - 1) % R);
+    if (s + R < total) advance();
+    wait_vmcnt<(R - 2) * PER>();  // this wave's loads of stage s + 1
+    barrier();
+    // MFMA phase
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j][i], fb[j][t], acc[i][t], 0, 0, 0);
+    if (++kk == KS) {
+      kk = 0;
+      // tile done: D[n][m], lane holds m = lane % 32 and four consecutive n per group
+      const int m0 = cc.mb * BM, n0 = cc.nb * BN;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int m = m0 + (grp * TM + t) * 32 + fr;
+        if (GLU && m < cc.cnt) {
+          // elements 4q + u (q = 0, 1): W half of unit 8q + 4h + u of the 32-row
+          // tile's 16 units; elements 4q + 8 + u: the V half of the same unit
+          bf16_t* orow = out + (static_cast<int64_t>(cc.e) * C + m) * (N >> 1);
+#pragma unroll
+          for (int i = 0; i < TN; ++i) {
+            const int nt0 = n0 + (wn * TN + i) * 32;
+            if (nt0 < N) {
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                float h[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) h[u] = apply_act<ACT>(acc[i][t][4 * q + u]) * acc[i][t][4 * q + 8 + u];
+                uint2 v;
+                v.x = pack_bf16x2(h[0], h[1]);
+                v.y = pack_bf16x2(h[2], h[3]);
+                *reinterpret_cast<uint2*>(orow + (nt0 >> 1) + 8 * q + 4 * half) = v;
+              }
+            }
+          }
+        } else if (m < cc.cnt) {
+          bf16_t* orow = out + (static_cast<int64_t>(cc.e) * C + m) * N;
+#pragma unroll
+          for (int i = 0; i < TN; ++i) {
+            const int nt0 = n0 + (wn * TN + i) * 32;
+            if (nt0 < N) {  // N % 32 == 0: a 32-column tile is wholly valid or not
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int n = nt0 + 8 * q + 4 * half;
+                uint2 v;
+                v.x = pack_bf16x2(apply_act<ACT>(acc[i][t][4 * q]), apply_act<ACT>(acc[i][t][4 * q + 1]));
+                v.y = pack_bf16x2(apply_act<ACT>(acc[i][t][4 * q + 2]), apply_act<ACT>(acc[i][t][4 * q + 3]));
+                *reinterpret_cast<uint2*>(orow + n) = v;
+              }
+            }
+          }
+        }
+      }
+      cc = step(cc);
+      zero_acc();
+    }
+    barrier();
+  }
+  if (grp == 0) barrier();
+  wait_vmcnt<0>();  // the last stages' repeated loads land before the block's LDS is released
 }
 
 // ---------------------------------------------------------------------------
@@ -856,6 +1109,23 @@ static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
   return hipGetLastError();
 }
 
+template <int ACT, bool GLU>
+static hipError_t run_pp(int E, const bf16_t* A, const bf16_t* W, bf16_t* out, const int32_t* count,
+                         int64_t C, int N, int K, hipStream_t s) {
+  auto kern = ffn_pp_bf16_kernel<ACT, GLU>;
+  constexpr int lds = ffn_pp_lds_bytes();
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err != hipSuccess) return err;
+  const int64_t tiles = static_cast<int64_t>(E) * ((C + kPpBM - 1) / kPpBM) * ((N + kPpBN - 1) / kPpBN);
+  if (tiles == 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>(tiles, 256);  // one persistent block per CU
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), lds, s, A, W, out, count, E,
+                     C, N, K);
+  return hipGetLastError();
+}
+
 template <int ACT, int NH, int S>
 static hipError_t run_fused(const Plan& p, int nspl, const bf16_t* A, const bf16_t* W1,
                             const bf16_t* W2, bf16_t* out, const int32_t* count, hipStream_t s) {
@@ -892,19 +1162,24 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // balance the CUs and keep three stages of a cold weight stream in flight
 // (Switch-Base down-projection inside the forward: 128-130 us, against 137 us
 // for 384-row tiles with a 2-stage ring and 140 us for 256-row tiles).
-// Capacity > 384: the same persistent ring with 256 x 256 tiles (8 waves of
-// 4 x 2 MFMA tiles, 2-stage ring of 64 KB stages; each weight tile is read by
-// every 256-row block of its expert, so those loads stay temporal).  Capacity
-// 161..384: the LDS-tiled 128 x 128 kernel, which wastes less on a partly
-// filled last row block (measured at capacity 320).  The ring kernel addresses
-// inside one expert with 32-bit offsets; larger experts take the LDS-tiled one.
-// N is the number of weight rows (2 d_ff for the GLU up-projection).
+// Capacity > 384 (MFMA-bound: each weight tile is read by every 256-row block of
+// its expert, so those loads stay temporal), 256 x 256 tiles: with a contraction
+// of at least 2048 the ping-pong kernel (X-MoE top-2 down-projection, K = 4096:
+// 380 us against 402 us for the ring); shorter contractions, where a tile's
+// epilogue is a larger share of its time, the ring with 8 waves of 4 x 2 MFMA
+// tiles and a 2-stage ring of 64 KB stages (X-MoE up-projection, K = 1024: 410
+// us against 443 us for ping-pong).  Capacity 161..384: the LDS-tiled 128 x 128
+// kernel, which wastes less on a partly filled last row block (measured at
+// capacity 320).  The ring kernels address inside one expert with 32-bit
+// offsets; larger experts take the LDS-tiled one.  N is the number of weight
+// rows (2 d_ff for the GLU up-projection).
 template <int ACT, bool GLU = false>
 static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf16_t* out,
                             const int32_t* count, int N, int K, hipStream_t s) {
   const int64_t lim = int64_t(1) << 32;
   if (int64_t(N) * K >= lim || p.C * K >= lim)
     return run_bf16<128, 128, 2, 2, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C > 384 && K >= 2048) return run_pp<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C > 384) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
     return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);

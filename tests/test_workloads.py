@@ -3,6 +3,7 @@ import numpy as np
 import torch
 
 import moe_workloads as W
+from oracle import capacity
 
 
 def test_bf16_rounding_matches_torch():
@@ -55,3 +56,12 @@ def test_full_configs():
     wl = W.WORKLOADS["large_zipf_top2_bf16"]
     b = W.make_inputs(wl, with_weights=False)["bias"]
     np.testing.assert_allclose(b, -1.1 * np.log(np.arange(1, 257)), rtol=1e-7)
+
+
+def test_long_contraction_cases_keep_their_shape():
+    # capacity above 384 and a 2048-long contraction in the down- (first) and the
+    # GLU up-projection (second), with more than one 256-row block per expert
+    for name, k_len in (("longk_top2_bf16", "d_ff"), ("geglu_longk_bf16", "d_model")):
+        wl = W.TEST_WORKLOADS[name]
+        assert capacity(wl.T, wl.E, wl.k, wl.capacity_factor) > 384 and getattr(wl, k_len) >= 2048
+        assert wl.T * wl.k / wl.E > 256
