@@ -114,7 +114,7 @@ TEST_WORKLOADS = {
     "wide_top2_bf16": Workload("wide_top2_bf16", T=1200, d_model=384, d_ff=256, E=40, k=2,
                                capacity_factor=1.0, act="relu", dtype="bf16"),
     # gated-linear-unit experts, one per grouped-GEMM capacity range: C = 63 (384-row
-    # weight tiles), 100, 150, 230 (LDS-tiled), 500 (256 x 256 tiles), and float32
+    # weight tiles), 100, 150, 230 and 500 (256 x 256 tiles), and float32
     "geglu_wide_top1_bf16": Workload("geglu_wide_top1_bf16", T=1500, d_model=768, d_ff=384, E=24,
                                      k=1, capacity_factor=1.0, act="gelu", dtype="bf16", glu=True),
     "reglu_c100_bf16": Workload("reglu_c100_bf16", T=1000, d_model=256, d_ff=320, E=10, k=1,
@@ -127,11 +127,12 @@ TEST_WORKLOADS = {
                                 capacity_factor=1.0, act="relu", dtype="bf16", glu=True),
     "reglu_small_f32": Workload("reglu_small_f32", T=600, d_model=128, d_ff=192, E=8, k=1,
                                 capacity_factor=1.25, act="relu", dtype="f32", glu=True),
-    # capacity > 384 with a contraction of 2048: the down-projection (K = d_ff) of a
-    # top-2 GELU layer with 128 output columns (half a 256-row weight tile), and the
-    # GeGLU up-projection (K = d_model) with two 256-row blocks per expert
+    # capacities above 160 with a contraction of 2048: the down-projection (K = d_ff)
+    # of a top-2 GELU layer at capacity 315 (every expert full, two 256-row blocks)
+    # with 128 output columns (half a 256-row weight tile), and the GeGLU
+    # up-projection (K = d_model) at capacity 480
     "longk_top2_bf16": Workload("longk_top2_bf16", T=900, d_model=128, d_ff=2048, E=4, k=2,
-                                capacity_factor=1.0, act="gelu", dtype="bf16"),
+                                capacity_factor=0.7, act="gelu", dtype="bf16"),
     "geglu_longk_bf16": Workload("geglu_longk_bf16", T=900, d_model=2048, d_ff=192, E=3, k=1,
                                  capacity_factor=1.6, act="gelu", dtype="bf16", glu=True),
 }

@@ -1162,31 +1162,30 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // balance the CUs and keep three stages of a cold weight stream in flight
 // (Switch-Base down-projection inside the forward: 128-130 us, against 137 us
 // for 384-row tiles with a 2-stage ring and 140 us for 256-row tiles).
-// Capacity > 384 (MFMA-bound: each weight tile is read by every 256-row block of
+// Capacity > 160 (MFMA-bound: each weight tile is read by every 256-row block of
 // its expert, so those loads stay temporal), 256 x 256 tiles: with a contraction
 // of at least 2048 the ping-pong kernel (X-MoE top-2 down-projection, K = 4096:
-// 380 us against 402 us for the ring); shorter contractions, where a tile's
-// epilogue is a larger share of its time, the ring with 8 waves of 4 x 2 MFMA
-// tiles and a 2-stage ring of 64 KB stages (X-MoE up-projection, K = 1024: 410
-// us against 443 us for ping-pong).  Capacity 161..384: the LDS-tiled 128 x 128
-// kernel, which wastes less on a partly filled last row block (measured at
-// capacity 320).  The ring kernels address inside one expert with 32-bit
-// offsets; larger experts take the LDS-tiled one.  N is the number of weight
-// rows (2 d_ff for the GLU up-projection).
+// 380 us against 402 us for the ring; large Zipf layer, capacity 320: 3.44 /
+// 3.21 ms up / down against 3.70 / 3.46 ms for the LDS-tiled 128 x 128 kernel);
+// shorter contractions, where a tile's epilogue is a larger share of its time,
+// the ring with 8 waves of 4 x 2 MFMA tiles and a 2-stage ring of 64 KB stages
+// (X-MoE up-projection, K = 1024: 410 us against 443 us for ping-pong).  The
+// ring kernels address inside one expert with 32-bit offsets; larger experts
+// take the LDS-tiled one.  N is the number of weight rows (2 d_ff for the GLU
+// up-projection).
 template <int ACT, bool GLU = false>
 static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf16_t* out,
                             const int32_t* count, int N, int K, hipStream_t s) {
   const int64_t lim = int64_t(1) << 32;
   if (int64_t(N) * K >= lim || p.C * K >= lim)
     return run_bf16<128, 128, 2, 2, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C > 384 && K >= 2048) return run_pp<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C > 384) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C > 160 && K >= 2048) return run_pp<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C > 160) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
     return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 128) return run_ring<4, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C <= 160) return run_ring<5, 2, 1, 4, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-  return run_bf16<128, 128, 2, 2, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  return run_ring<5, 2, 1, 4, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
 }
 
 // Column groups per expert for the fused FFN, or 0 where it does not apply:
