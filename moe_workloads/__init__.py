@@ -135,6 +135,13 @@ TEST_WORKLOADS = {
                                 capacity_factor=0.7, act="gelu", dtype="bf16"),
     "geglu_longk_bf16": Workload("geglu_longk_bf16", T=900, d_model=2048, d_ff=192, E=3, k=1,
                                  capacity_factor=1.6, act="gelu", dtype="bf16", glu=True),
+    # 2048 x 2048 projections at capacity 315 (three 128-row blocks, the last one
+    # ragged): both GEMMs of the plain layer and the GLU up-projection of the second
+    # (2 x 1024 w1 rows) have at least four 512-row column blocks
+    "wide_longk_bf16": Workload("wide_longk_bf16", T=700, d_model=2048, d_ff=2048, E=2, k=1,
+                                capacity_factor=0.9, act="gelu", dtype="bf16"),
+    "geglu_wide_longk_bf16": Workload("geglu_wide_longk_bf16", T=700, d_model=2048, d_ff=1024, E=2,
+                                      k=1, capacity_factor=0.9, act="gelu", dtype="bf16", glu=True),
 }
 
 

@@ -528,18 +528,17 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
 // final stage into free slots, so every memory phase issues the same loads and
 // waits on one fixed memory-counter threshold.
 // ---------------------------------------------------------------------------
-constexpr int kPpBM = 256, kPpBN = 256, kPpBK = 32, kPpSlots = 4;
-
+// TM x TN MFMA tiles per wave (activation, weight), R ring slots of 32-k stages.
+template <int TM, int TN, int R>
 __host__ __device__ constexpr int ffn_pp_lds_bytes() {
-  return kPpSlots * (kPpBM + kPpBN) * kPpBK * 2 + (2 * kMaxE + 1) * 4;
+  return R * (2 * TM * 32 + 4 * TN * 32) * 32 * 2 + (2 * kMaxE + 1) * 4;
 }
 
-template <int ACT, bool GLU>
+template <int TM, int TN, int R, int ACT, bool GLU>
 __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
     const int32_t* __restrict__ count, int E, int64_t C, int N, int K) {
-  constexpr int BM = kPpBM, BN = kPpBN, BK = kPpBK, R = kPpSlots;
-  constexpr int TM = 4, TN = 2;          // MFMA tiles per wave (activation, weight)
+  constexpr int BM = 2 * TM * 32, BN = 4 * TN * 32, BK = 32;
   constexpr int RB = BK * 2;             // LDS row bytes
   constexpr int CPR = BK / 8;            // 16-byte chunks per row
   constexpr int RPI = 1024 / RB;         // rows per wave instruction
@@ -547,7 +546,7 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
   constexpr int AL = BM / RPI / 8;       // activation instructions per wave per stage
   constexpr int PER = WL + AL;
   constexpr int STAGE = (BN + BM) * RB;
-  static_assert(BM == 2 * TM * 32 && BN == 4 * TN * 32, "wave grid");
+  static_assert(BN % (RPI * 8) == 0 && BM % (RPI * 8) == 0 && R >= 3, "stage split");
   extern __shared__ __align__(16) unsigned char smem[];
   int* pre = reinterpret_cast<int*>(smem + R * STAGE);  // [E + 1] tile prefix per expert
   int* cnts = pre + kMaxE + 1;                            // [E] clamped row counts
@@ -1109,16 +1108,17 @@ static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
   return hipGetLastError();
 }
 
-template <int ACT, bool GLU>
+template <int TM, int TN, int R, int ACT, bool GLU>
 static hipError_t run_pp(int E, const bf16_t* A, const bf16_t* W, bf16_t* out, const int32_t* count,
                          int64_t C, int N, int K, hipStream_t s) {
-  auto kern = ffn_pp_bf16_kernel<ACT, GLU>;
-  constexpr int lds = ffn_pp_lds_bytes();
+  auto kern = ffn_pp_bf16_kernel<TM, TN, R, ACT, GLU>;
+  constexpr int lds = ffn_pp_lds_bytes<TM, TN, R>();
+  constexpr int BM = 2 * TM * 32, BN = 4 * TN * 32;
   static_assert(lds <= 160 * 1024, "LDS budget");
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
-  const int64_t tiles = static_cast<int64_t>(E) * ((C + kPpBM - 1) / kPpBM) * ((N + kPpBN - 1) / kPpBN);
+  const int64_t tiles = static_cast<int64_t>(E) * ((C + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
   const int64_t grid = std::min<int64_t>(tiles, 256);  // one persistent block per CU
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), lds, s, A, W, out, count, E,
@@ -1162,14 +1162,19 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // balance the CUs and keep three stages of a cold weight stream in flight
 // (Switch-Base down-projection inside the forward: 128-130 us, against 137 us
 // for 384-row tiles with a 2-stage ring and 140 us for 256-row tiles).
-// Capacity > 160 (MFMA-bound: each weight tile is read by every 256-row block of
-// its expert, so those loads stay temporal), 256 x 256 tiles: with a contraction
-// of at least 2048 the ping-pong kernel (X-MoE top-2 down-projection, K = 4096:
-// 380 us against 402 us for the ring; large Zipf layer, capacity 320: 3.44 /
-// 3.21 ms up / down against 3.70 / 3.46 ms for the LDS-tiled 128 x 128 kernel);
-// shorter contractions, where a tile's epilogue is a larger share of its time,
-// the ring with 8 waves of 4 x 2 MFMA tiles and a 2-stage ring of 64 KB stages
-// (X-MoE up-projection, K = 1024: 410 us against 443 us for ping-pong).  The
+// Capacity > 160 (MFMA-bound: each weight tile is read by every row block of its
+// expert, so those loads stay temporal).  With a contraction of at least 2048 the
+// ping-pong kernel: 128 x 512 tiles (3-slot ring) where N holds at least four
+// 512-row column blocks, so that a partly filled last row block wastes at most
+// 127 rows (large Zipf layer, capacity 320, counts 162..320: 3.24 / 3.12 ms up /
+// down against 3.47 / 3.25 ms for 256 x 256 tiles and 3.70 / 3.46 ms for the
+// LDS-tiled 128 x 128 kernel), else 256 x 256 tiles (X-MoE top-2
+// down-projection, N = 1024, K = 4096: 380 us against 451 us for 128 x 512,
+// whose 578 long tiles balance poorly over 256 CUs, and 402 us for the ring).
+// Shorter contractions, where a tile's epilogue is a larger share of its time:
+// the ring with 256 x 256 tiles, 8 waves of 4 x 2 MFMA tiles and a 2-stage ring
+// of 64 KB stages (X-MoE up-projection, K = 1024: 410 us against 443 us for
+// ping-pong).  The
 // ring kernels address inside one expert with 32-bit offsets; larger experts
 // take the LDS-tiled one.  N is the number of weight rows (2 d_ff for the GLU
 // up-projection).
@@ -1179,7 +1184,9 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
   const int64_t lim = int64_t(1) << 32;
   if (int64_t(N) * K >= lim || p.C * K >= lim)
     return run_bf16<128, 128, 2, 2, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C > 160 && K >= 2048) return run_pp<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C > 160 && K >= 2048 && N >= 2048)
+    return run_pp<2, 4, 3, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C > 160 && K >= 2048) return run_pp<4, 2, 4, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C > 160) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
     return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);

@@ -68,3 +68,13 @@ def test_long_contraction_cases_keep_their_shape():
         c = capacity(wl.T, wl.E, wl.k, wl.capacity_factor)
         assert lo <= c <= hi and getattr(wl, k_len) >= 2048
         assert min(c, wl.T * wl.k / wl.E) > 256
+
+
+def test_wide_long_contraction_cases_keep_their_shape():
+    # N >= 2048 and K >= 2048 in the named GEMMs at a capacity in 161..384 with a
+    # ragged last 128-row block
+    for name in ("wide_longk_bf16", "geglu_wide_longk_bf16"):
+        wl = W.TEST_WORKLOADS[name]
+        c = capacity(wl.T, wl.E, wl.k, wl.capacity_factor)
+        assert 161 <= c <= 384 and c % 128 != 0 and wl.T * wl.k / wl.E > c
+        assert wl.d_model >= 2048 and W.w1_rows(wl) >= 2048
