@@ -1,0 +1,99 @@
+"""GPU parity of the grouped expert GEMMs alone (moe_expert_up, moe_expert_down).
+
+The layer tests reach every GEMM kernel, but at their sizes each persistent
+block of the large-capacity kernels gets at most one tile.  Here the expert
+batches are synthetic (x_e filled with the seeded dyadic rows of a layer of the
+same shape, per-expert row counts chosen by hand: empty experts, one row, rows
+on both sides of the 128- and 256-row block edges, full capacity), sized so
+that there are more tiles than blocks and every block walks several tiles of
+several experts.  Sampled rows of H and y_e are compared with the oracle's
+expert FFN (Switch notes 2.1; MosaicBERT review for GLU) on the same rows: H
+within the bf16 output tolerance, y_e from the oracle's H likewise (the GPU's
+y_e is computed from its bf16-rounded H).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as W
+import sparse_mixture_experts_13_amd as moe
+import oracle
+from gpu_util import DEV, max_abs_rel, out_tol, to_dev, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+# (label, d_model, d_ff, E, capacity, glu); the kernel each projection takes
+# follows from the capacity (> 160), the contraction K and the output rows N.
+CASES = [
+    ("up ring 256x256 (K=1024), down ping-pong 256x256 (K=2048, N=1024)", 1024, 2048, 40, 600, False),
+    ("GLU up ring 256x256 (N=4096), down ping-pong 256x256", 1024, 2048, 40, 600, True),
+    ("up and down ping-pong 128x512 (K=N=2048)", 2048, 2048, 40, 300, False),
+    ("GLU up ping-pong 128x512 (K=N=2048), down ring 256x256 (K=1024)", 2048, 1024, 40, 300, True),
+]
+
+
+def _counts(E: int, C: int, seed: int) -> np.ndarray:
+    special = [0, 1, C, 127, 128, 129, 255, 256, 257, C - 1, 0, C]
+    rng = np.random.default_rng(seed)
+    c = [v for v in special if 0 <= v <= C]
+    while len(c) < E:
+        c.append(int(rng.integers(C // 2, C + 1)))
+    c = np.array(c[:E], dtype=np.int32)
+    rng.shuffle(c)
+    return c
+
+
+def _rows(n: int, rng) -> np.ndarray:
+    pick = {0, n - 1, min(n - 1, 127), min(n - 1, 128), min(n - 1, 255), min(n - 1, 256)}
+    pick |= set(rng.integers(0, n, 3).tolist())
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("label,d,f,E,C,glu", CASES, ids=[c[0] for c in CASES])
+def test_grouped_gemm_many_tiles(label, d, f, E, C, glu):
+    print(f"[gpu] grouped GEMM {label}", flush=True)
+    wl = W.Workload("gemm", T=E * C, d_model=d, d_ff=f, E=E, k=1, capacity_factor=1.0,
+                    act="gelu", dtype="bf16", glu=glu)
+    cfg = moe.config_for(wl)
+    assert moe.capacity(cfg) == C
+    counts = _counts(E, C, seed=E + C)
+    # more tiles than the 256 persistent blocks in both projections (counted in 256 x 256 tiles)
+    blocks = int(np.sum((counts + 255) // 256))
+    assert blocks * (W.w1_rows(wl) // 256) > 256 and blocks * (d // 256) > 256
+
+    x = W.make_inputs(wl, with_weights=False)["x"].reshape(E, C, d)  # bf16 bits, dyadic
+    w1 = torch.empty((E, W.w1_rows(wl), d), dtype=torch.bfloat16, device=DEV)
+    w2 = torch.empty((E, d, f), dtype=torch.bfloat16, device=DEV)
+    host = {}
+
+    def put(e, a, b):
+        w1[e].copy_(to_dev(a))
+        w2[e].copy_(to_dev(b))
+        host[e] = (a, b)
+
+    W.for_each_expert(wl, put, threads=8)
+    x_e = to_dev(x)
+    cnt = to_dev(counts)
+    hidden = torch.zeros((E, C, f), dtype=torch.bfloat16, device=DEV)
+    y_e = torch.zeros((E, C, d), dtype=torch.bfloat16, device=DEV)
+    moe.expert_up(cfg, x_e, cnt, w1, hidden)
+    moe.expert_down(cfg, hidden, cnt, w2, y_e)
+    torch.cuda.synchronize()
+    h_got = to_host_f64(hidden)
+    y_got = to_host_f64(y_e)
+
+    rng = np.random.default_rng(7)
+    tol = out_tol(wl)
+    for e in range(E):
+        n = int(counts[e])
+        if n == 0:
+            continue
+        r = _rows(n, rng)
+        xr = oracle.as_f64(x[e, r])
+        w1e, w2e = host[e]
+        h_ref = oracle.expert_hidden(xr, w1e, wl.act, glu)
+        err = max_abs_rel(h_got[e, r], h_ref)
+        assert err <= tol, f"{label}: H expert {e} (count {n}) rows {r.tolist()}: {err:.3g}"
+        y_ref = oracle.expert_apply(xr, w1e, w2e, wl.act, glu)
+        err = max_abs_rel(y_got[e, r], y_ref)
+        assert err <= tol, f"{label}: y_e expert {e} (count {n}) rows {r.tolist()}: {err:.3g}"

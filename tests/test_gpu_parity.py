@@ -279,10 +279,10 @@ def test_capacity_one():
     assert (ref["expert_count"] <= 1).all()
 
 
-@pytest.mark.parametrize("cf,kernel", [(3.2, "LDS-tiled 128x128"), (1.0, "ring, 64-row blocks")])
+@pytest.mark.parametrize("cf,kernel", [(3.2, "ring, 256-row blocks"), (1.0, "ring, 64-row blocks")])
 def test_capacity_kernel_ranges(cf, kernel):
-    """Capacities that select the other grouped-GEMM kernels: 161..384 (C = 200 here)
-    and the smallest (C = 63)."""
+    """Capacities that select the other grouped-GEMM shapes: 161..384 with short
+    contractions (C = 200 here) and the smallest (C = 63)."""
     wl = W.TEST_WORKLOADS["switch_small_bf16"].replace(capacity_factor=cf)
     inputs = W.make_inputs(wl)
     ref, _ = _run_case(wl, inputs, f"C={oracle.capacity(wl.T, wl.E, wl.k, cf)} {kernel}")
