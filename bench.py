@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,7 +30,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 FP32_PEAK_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "sparse_mixture_experts_13_amd", "csrc", "expert_ffn.hip")
+KERNEL_SRC = [os.path.join(ROOT, "sparse_mixture_experts_13_amd", "csrc", name)
+              for name in ("expert_ffn.hip", "moe_common.h")]
 
 
 def parse():
@@ -47,9 +49,17 @@ def parse():
     return ap.parse_args()
 
 
-def source_sha(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(paths) -> str:
+    """sha256[:16] of the kernel code: the sources with // comments, trailing blanks
+    and empty lines removed, so that an edit of comments keeps the counters valid."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path) as f:
+            for line in f:
+                line = re.sub(r"//.*", "", line).rstrip()
+                if line:
+                    h.update((line + "\n").encode())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel: str, workload: str):

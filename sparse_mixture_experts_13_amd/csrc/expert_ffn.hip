@@ -8,10 +8,11 @@
 // [E][C][K], weights [E][N][K]).  The kernel computes the transposed tile
 // D = W . X^T so that each lane ends with four consecutive output columns of
 // one row (8-byte stores).  bf16 runs on v_mfma_f32_32x32x16_bf16 with float32
-// accumulation in a persistent kernel over the non-empty tiles only, so the
-// grid is fixed (no device-to-host read of the counts) while dropped or unused
-// capacity costs neither bandwidth nor MFMA work.  float32 workloads use a
-// plain float32 FMA tile kernel.
+// accumulation in persistent kernels over the non-empty tiles only (a stage
+// ring kernel, and a ping-pong kernel for MFMA-bound tiles with long
+// contractions), so the grid is fixed (no device-to-host read of the counts)
+// while dropped or unused capacity costs neither bandwidth nor MFMA work.
+// float32 workloads use a plain float32 FMA tile kernel.
 //
 // Gated-linear-unit experts (MosaicBERT review, methodology: GLU in the
 // feed-forward layer, in a fused form): H = act(x W) * (x V) with w1 = [W; V]
@@ -43,10 +44,11 @@ __host__ __device__ constexpr int ffn_lds_bytes() {
   return 2 * (BM + BN) * GLD * 2;
 }
 
-// LDS-tiled grouped GEMM for large capacities: one block per (expert, row
-// tile, column tile) of BM x BN, register-staged double-buffered LDS tiles
-// (BK = 64, rows padded to 144 bytes: conflict-free fragment reads); tiles past
-// the expert's count exit at once.
+// LDS-tiled grouped GEMM, for experts whose panels exceed 32-bit element offsets
+// (the persistent kernels address inside an expert with 32-bit offsets): one
+// block per (expert, row tile, column tile) of BM x BN, register-staged
+// double-buffered LDS tiles (BK = 64, rows padded to 144 bytes: conflict-free
+// fragment reads); tiles past the expert's count exit at once.
 template <int BM, int BN, int WM, int WN, int ACT, bool GLU>
 __global__ __launch_bounds__(256) void ffn_gemm_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
