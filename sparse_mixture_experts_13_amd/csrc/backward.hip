@@ -194,12 +194,6 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(
 // bf16(acc * act(za)) at out[m][N + n].
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float gelu_grad(float z) {
-  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
-  const float pdf = expf(-0.5f * z * z) * 0.39894228040143268f;
-  return fmaf(z, pdf, cdf);
-}
-
 template <int ROWS, bool KC, int BK>
 struct OpTile {
   // LDS elements per buffer: [ROWS][BK + 8] (k-contiguous) or [BK][ROWS + 8]
@@ -687,16 +681,19 @@ hipError_t expert_backward<bf16_t>(const Plan& p, const bf16_t* x_e, const bf16_
     else
       MOE_TRY((run_bgemm_rows<2, 1>(p, dy_e, sX, d, w2, sW, f, dz, sZ, r, z, count, Ci,
                                                       f, d, true, s)));
-  } else if (p.act == 0) {
-    MOE_TRY((run_bgemm_rows<1, 0>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
-                                                    f, d, true, s)));
   } else {
-    MOE_TRY((run_bgemm_rows<1, 1>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci,
-                                                    f, d, true, s)));
+    // the ping-pong GEMM where it applies (large capacities, d_model >= 2048)
+    hipError_t err = launch_bwd_rows_pp(p, dy_e, w2, dz, z, count, f, d, p.act, s);
+    if (err == hipErrorNotSupported)
+      err = p.act == 0 ? run_bgemm_rows<1, 0>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci, f, d, true, s)
+                       : run_bgemm_rows<1, 1>(p, dy_e, sX, d, w2, sW, f, dz, sH, f, z, count, Ci, f, d, true, s);
+    MOE_TRY(err);
   }
-  // dx_e[s][d] = sum_r dZ[s][r] w1[r][d]   (B = w1 [k=r][n=d])
-  MOE_TRY((run_bgemm_rows<0, 0>(p, dz, sZ, r, w1, sW1, d, dx_e, sX, d, nullptr, count,
-                                                  Ci, d, r, true, s)));
+  // dx_e[s][d] = sum_r dZ[s][r] w1[r][d]   (B = w1 [k=r][n=d]); ping-pong where it applies
+  hipError_t err = launch_bwd_rows_pp(p, dz, w1, dx_e, nullptr, count, d, r, -1, s);
+  if (err == hipErrorNotSupported)
+    err = run_bgemm_rows<0, 0>(p, dz, sZ, r, w1, sW1, d, dx_e, sX, d, nullptr, count, Ci, d, r, true, s);
+  MOE_TRY(err);
   // dw2[d][f] = sum_s dy_e[s][d] H[s][f]   (A = dy_e [k=s][m=d], B = H [k=s][n=f])
   MOE_TRY((run_bgemm<128, 128, 32, false, false, 0, 0>(p, dy_e, sX, d, hidden, sH, f, dw2, sW, f, nullptr,
                                                     count, d, f, 0, false, s)));

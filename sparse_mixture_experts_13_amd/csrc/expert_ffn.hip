@@ -509,26 +509,33 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
 // Ping-pong grouped GEMM for large capacities, where a tile re-reads its weight
 // rows for several row blocks and the MFMA pipe, not HBM, sets the pace.
 //
-// Block tile: 256 activation rows x 256 weight rows, persistent blocks of 8
-// waves in two groups of four (waves w and w + 4 share a SIMD).  Wave (g, wn)
-// owns activation rows 128 g .. 128 g + 127 and weight rows 64 wn .. 64 wn + 63
-// of the tile: 4 x 2 MFMA tiles of 32 x 32.  The k loop runs in 32-k stages
-// through a 4-slot direct-to-LDS ring (32 KB a stage), and every stage has two
+// Block tile: BM = 64 TM activation rows x BN = 128 TN weight rows (256 x 256 or
+// 128 x 512), persistent blocks of 8 waves in two groups of four (waves w and
+// w + 4 share a SIMD).  Wave (g, wn) owns activation rows g BM / 2 .. and weight
+// rows wn BN / 4 .. of the tile: TM x TN MFMA tiles of 32 x 32.  The k loop runs
+// in 32-k stages through an R-slot direct-to-LDS ring, and every stage has two
 // phases separated by block barriers:
-//   * memory phase: read the wave's 12 fragments of the stage from LDS, issue
-//     its 4 direct-to-LDS loads of the stage three ahead, wait for its own
-//     loads of the next stage;
+//   * memory phase: read the wave's fragments of the stage from LDS, issue its
+//     direct-to-LDS loads of the stage R - 1 ahead, wait for its own loads of
+//     the next stage;
 //   * MFMA phase: 16 MFMAs on the fragments in registers (and the tile's
 //     epilogue after its last stage).
 // Group 1 runs one phase behind group 0, so on every SIMD one wave issues
 // MFMAs while the other feeds LDS and memory: the matrix pipe never waits for
-// a fragment read or a barrier of its own wave.  A stage's loads are issued
-// three stages before its first reader and waited for one stage before, so
-// about 64 KB per CU are in flight.  Tiles (expert, row block, column block),
-// the per-XCD strided share of them and the clamped rows past the count are as
-// in the ring kernel above; the loads of the block's last stages re-read its
-// final stage into free slots, so every memory phase issues the same loads and
-// waits on one fixed memory-counter threshold.
+// a fragment read or a barrier of its own wave.  Tiles (expert, row block,
+// column block), the per-XCD strided share of them and the clamped rows past
+// the count are as in the ring kernel above; the loads of the block's last
+// stages re-read its final stage into free slots, so every memory phase issues
+// the same loads and waits on one fixed memory-counter threshold.
+// BT: the second operand is stored [K][N] per expert (row pitch N) instead of
+// [N][K] -- the weights of the backward's token-row products dZ = dy_e w2 and
+// dx_e = dZ w1.  Its stage tile is then [32 k rows][BN] and its fragments come
+// from two LDS transpose reads (ds_read_b64_tr_b16: within each 16-lane group,
+// lane i receives element i % 4 of the 8-byte chunks addressed by lanes
+// 4 q + i / 4); the 16-byte chunk c of k row r sits at chunk position
+// c ^ 4 (r mod 4), so that every 32 lanes of a transpose read hit 32 distinct
+// 8-byte bank slots.  EPI 1 multiplies the product by act'(z), z read from
+// `aux` at the output position (the backward's dZ).
 // ---------------------------------------------------------------------------
 // TM x TN MFMA tiles per wave (activation, weight), R ring slots of 32-k stages.
 template <int TM, int TN, int R>
@@ -536,11 +543,13 @@ __host__ __device__ constexpr int ffn_pp_lds_bytes() {
   return R * (2 * TM * 32 + 4 * TN * 32) * 32 * 2 + (2 * kMaxE + 1) * 4;
 }
 
-template <int TM, int TN, int R, int ACT, bool GLU>
+template <int TM, int TN, int R, int ACT, bool GLU, bool BT = false, int EPI = 0>
 __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
-    const int32_t* __restrict__ count, int E, int64_t C, int N, int K) {
+    const int32_t* __restrict__ count, int E, int64_t C, int N, int K, const bf16_t* __restrict__ aux) {
+  static_assert(!(BT && GLU) && (EPI == 0 || (EPI == 1 && !GLU)), "operand and epilogue forms");
   constexpr int BM = 2 * TM * 32, BN = 4 * TN * 32, BK = 32;
+  constexpr int KRB = BN * 2;            // BT: bytes per k row of the weight stage tile
   constexpr int RB = BK * 2;             // LDS row bytes
   constexpr int CPR = BK / 8;            // 16-byte chunks per row
   constexpr int RPI = 1024 / RB;         // rows per wave instruction
@@ -621,11 +630,18 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
 #pragma unroll
     for (int q = 0; q < WL; ++q) {
       const int p = (wave * WL + q) * 64 + lane;
-      const int row = p / CPR;
-      const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
-      int wr = min(lc.nb * BN + row, N - 1);
-      if constexpr (GLU) wr = glu_row(wr, N >> 1);
-      const uint32_t off = static_cast<uint32_t>(wr) * K + lk * BK + c * 8;
+      uint32_t off;
+      if constexpr (BT) {  // 16-byte chunk p of the [32][BN] tile: k row p / (BN / 8)
+        const int kr = p / (BN / 8);
+        const int c = (p % (BN / 8)) ^ (4 * (kr & 3));
+        off = static_cast<uint32_t>(lk * BK + kr) * N + min(lc.nb * BN + c * 8, N - 8);
+      } else {
+        const int row = p / CPR;
+        const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
+        int wr = min(lc.nb * BN + row, N - 1);
+        if constexpr (GLU) wr = glu_row(wr, N >> 1);
+        off = static_cast<uint32_t>(wr) * K + lk * BK + c * 8;
+      }
       __builtin_amdgcn_global_load_lds(We + off, (lds_void*)(base + (wave * WL + q) * 1024), 16, 0, 0);
     }
 #pragma unroll
@@ -686,8 +702,25 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
       }
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
-        const int row = (wn * TN + i) * 32 + fr;
-        fa[j][i] = *reinterpret_cast<const bf16x8*>(sw + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
+        if constexpr (BT) {
+          // lane 16 g + 4 q + c' reads k row 16 j + 8 (g / 2) + q (+ 4) at column
+          // (wn TN + i) 32 + 16 (g % 2) + 4 c'; every lane ends with its own column
+          // (row fr of the fragment) at k = 16 j + 8 half .. + 7
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+          const int trg = lane >> 4;
+          const int kr = 16 * j + 8 * (trg >> 1) + ((lane & 15) >> 2);
+          const int x = (wn * TN + i) * 32 + 16 * (trg & 1) + 4 * (lane & 3);
+          const int cpos = (((x >> 3) ^ (4 * (kr & 3))) << 4) + (x & 7) * 2;  // same for kr + 4
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sw + kr * KRB + cpos));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sw + (kr + 4) * KRB + cpos));
+          typedef short s16x8 __attribute__((ext_vector_type(8)));
+          const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          fa[j][i] = __builtin_bit_cast(bf16x8, v);
+        } else {
+          const int row = (wn * TN + i) * 32 + fr;
+          fa[j][i] = *reinterpret_cast<const bf16x8*>(sw + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
+        }
       }
     }
     issue_stage((s + R - 1) % R);
@@ -738,9 +771,21 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 const int n = nt0 + 8 * q + 4 * half;
+                float h[4];
+                if constexpr (EPI == 1) {  // acc * act'(z), z at the output position
+                  const uint2 zz = *reinterpret_cast<const uint2*>(
+                      aux + (static_cast<int64_t>(cc.e) * C + m) * N + n);
+                  const float z[4] = {__uint_as_float(zz.x << 16), __uint_as_float(zz.x & 0xFFFF0000u),
+                                      __uint_as_float(zz.y << 16), __uint_as_float(zz.y & 0xFFFF0000u)};
+#pragma unroll
+                  for (int u = 0; u < 4; ++u) h[u] = acc[i][t][4 * q + u] * act_grad<ACT>(z[u]);
+                } else {
+#pragma unroll
+                  for (int u = 0; u < 4; ++u) h[u] = apply_act<ACT>(acc[i][t][4 * q + u]);
+                }
                 uint2 v;
-                v.x = pack_bf16x2(apply_act<ACT>(acc[i][t][4 * q]), apply_act<ACT>(acc[i][t][4 * q + 1]));
-                v.y = pack_bf16x2(apply_act<ACT>(acc[i][t][4 * q + 2]), apply_act<ACT>(acc[i][t][4 * q + 3]));
+                v.x = pack_bf16x2(h[0], h[1]);
+                v.y = pack_bf16x2(h[2], h[3]);
                 *reinterpret_cast<uint2*>(orow + n) = v;
               }
             }
@@ -1110,10 +1155,10 @@ static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
   return hipGetLastError();
 }
 
-template <int TM, int TN, int R, int ACT, bool GLU>
+template <int TM, int TN, int R, int ACT, bool GLU, bool BT = false, int EPI = 0>
 static hipError_t run_pp(int E, const bf16_t* A, const bf16_t* W, bf16_t* out, const int32_t* count,
-                         int64_t C, int N, int K, hipStream_t s) {
-  auto kern = ffn_pp_bf16_kernel<TM, TN, R, ACT, GLU>;
+                         int64_t C, int N, int K, hipStream_t s, const bf16_t* aux = nullptr) {
+  auto kern = ffn_pp_bf16_kernel<TM, TN, R, ACT, GLU, BT, EPI>;
   constexpr int lds = ffn_pp_lds_bytes<TM, TN, R>();
   constexpr int BM = 2 * TM * 32, BN = 4 * TN * 32;
   static_assert(lds <= 160 * 1024, "LDS budget");
@@ -1124,7 +1169,7 @@ static hipError_t run_pp(int E, const bf16_t* A, const bf16_t* W, bf16_t* out, c
   if (tiles == 0) return hipSuccess;
   const int64_t grid = std::min<int64_t>(tiles, 256);  // one persistent block per CU
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), lds, s, A, W, out, count, E,
-                     C, N, K);
+                     C, N, K, aux);
   return hipGetLastError();
 }
 
@@ -1258,6 +1303,26 @@ hipError_t launch_expert_up_act(const Plan& p, const void* x_e, const int32_t* e
                       static_cast<float*>(out), expert_count, p.C, f, d, s);
   }
   return launch_expert_up(q, x_e, expert_count, w1, out, s);
+}
+
+// The backward's token-row products on the ping-pong kernel (second operand
+// stored [K][N]), under the forward's rule for it: capacity > 160 and K >= 2048,
+// 128 x 512 tiles where N >= 2048, else 256 x 256; hipErrorNotSupported elsewhere.
+hipError_t launch_bwd_rows_pp(const Plan& p, const bf16_t* A, const bf16_t* B, bf16_t* out,
+                              const bf16_t* aux, const int32_t* count, int N, int K, int grad_act,
+                              hipStream_t s) {
+  const int64_t lim = int64_t(1) << 32;
+  if (p.dtype != 1 || p.C <= 160 || K < 2048 || int64_t(N) * K >= lim || p.C * K >= lim)
+    return hipErrorNotSupported;
+  const bool wide = N >= 2048;
+  if (grad_act < 0)
+    return wide ? run_pp<2, 4, 3, 2, false, true, 0>(p.E, A, B, out, count, p.C, N, K, s)
+                : run_pp<4, 2, 4, 2, false, true, 0>(p.E, A, B, out, count, p.C, N, K, s);
+  if (grad_act == 0)
+    return wide ? run_pp<2, 4, 3, 0, false, true, 1>(p.E, A, B, out, count, p.C, N, K, s, aux)
+                : run_pp<4, 2, 4, 0, false, true, 1>(p.E, A, B, out, count, p.C, N, K, s, aux);
+  return wide ? run_pp<2, 4, 3, 1, false, true, 1>(p.E, A, B, out, count, p.C, N, K, s, aux)
+              : run_pp<4, 2, 4, 1, false, true, 1>(p.E, A, B, out, count, p.C, N, K, s, aux);
 }
 
 hipError_t launch_expert_down(const Plan& p, const void* hidden, const int32_t* expert_count,

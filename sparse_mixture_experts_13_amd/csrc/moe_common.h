@@ -108,6 +108,19 @@ template <int ACT> __device__ __forceinline__ float apply_act(float z) {
   else return z;
 }
 
+// d/dz of GELU: Phi(z) + z phi(z), with the library erff and expf.
+__device__ __forceinline__ float gelu_grad(float z) {
+  const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
+  const float pdf = expf(-0.5f * z * z) * 0.39894228040143268f;
+  return fmaf(z, pdf, cdf);
+}
+
+// act'(z): ReLU's derivative (0 at the kink) or GELU's.
+template <int ACT> __device__ __forceinline__ float act_grad(float z) {
+  if constexpr (ACT == 0) return z > 0.f ? 1.f : 0.f;
+  else return gelu_grad(z);
+}
+
 // Wave-wide reductions (wave64) built on cross-lane shuffles.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

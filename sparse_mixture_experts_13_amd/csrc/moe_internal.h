@@ -68,6 +68,13 @@ hipError_t launch_expert_down(const Plan& p, const void* hidden, const int32_t* 
 // Up-projection with an explicit activation (2: none, for the pre-activation).
 hipError_t launch_expert_up_act(const Plan& p, const void* x_e, const int32_t* expert_count,
                                 const void* w1, void* out, int act, hipStream_t s);
+// Backward token-row product out[e][m][n] = sum_k A[e][m][k] B[e][k][n] (A [C][K],
+// B [K][N], out [C][N] per expert; rows m < count[e]) on the ping-pong GEMM, times
+// act'(aux[e][m][n]) for grad_act 0 (ReLU) or 1 (GELU), plain for grad_act -1.
+// hipErrorNotSupported where that kernel does not apply (the caller falls back).
+hipError_t launch_bwd_rows_pp(const Plan& p, const uint16_t* A, const uint16_t* B, uint16_t* out,
+                              const uint16_t* aux, const int32_t* count, int N, int K, int grad_act,
+                              hipStream_t s);
 
 // backward.hip
 constexpr int kBwdSplit = 64;  // token ranges of the router weight gradient
