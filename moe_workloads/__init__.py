@@ -142,6 +142,10 @@ TEST_WORKLOADS = {
                                 capacity_factor=0.9, act="gelu", dtype="bf16"),
     "geglu_wide_longk_bf16": Workload("geglu_wide_longk_bf16", T=700, d_model=2048, d_ff=1024, E=2,
                                       k=1, capacity_factor=0.9, act="gelu", dtype="bf16", glu=True),
+    # capacity 100 with d_model 1024 and d_ff 2048: the backward's dZ product (K = 1024,
+    # N = 2048) on the ping-pong GEMM at a capacity below 161
+    "mid_wide_bf16": Workload("mid_wide_bf16", T=600, d_model=1024, d_ff=2048, E=6, k=1,
+                              capacity_factor=1.0, act="gelu", dtype="bf16"),
 }
 
 

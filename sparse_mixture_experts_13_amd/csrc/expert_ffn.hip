@@ -1306,15 +1306,18 @@ hipError_t launch_expert_up_act(const Plan& p, const void* x_e, const int32_t* e
 }
 
 // The backward's token-row products on the ping-pong kernel (second operand
-// stored [K][N]), under the forward's rule for it: capacity > 160 and K >= 2048,
-// 128 x 512 tiles where N >= 2048, else 256 x 256; hipErrorNotSupported elsewhere.
+// stored [K][N]): contractions of at least 1024, 128 x 512 tiles where N >= 2048
+// and the capacity exceeds 64 (RRE 4x16 backward, capacity 160: 5.96 -> 5.54 ms),
+// 256 x 256 tiles where the capacity exceeds 160 (X-MoE top-2: 3.12 -> 2.92 ms,
+// large Zipf layer 24.2 -> 22.7 ms, against the LDS-tiled backward GEMM);
+// hipErrorNotSupported elsewhere (the caller falls back to that kernel).
 hipError_t launch_bwd_rows_pp(const Plan& p, const bf16_t* A, const bf16_t* B, bf16_t* out,
                               const bf16_t* aux, const int32_t* count, int N, int K, int grad_act,
                               hipStream_t s) {
   const int64_t lim = int64_t(1) << 32;
-  if (p.dtype != 1 || p.C <= 160 || K < 2048 || int64_t(N) * K >= lim || p.C * K >= lim)
-    return hipErrorNotSupported;
   const bool wide = N >= 2048;
+  if (p.dtype != 1 || K < 1024 || p.C <= (wide ? 64 : 160) || int64_t(N) * K >= lim || p.C * K >= lim)
+    return hipErrorNotSupported;
   if (grad_act < 0)
     return wide ? run_pp<2, 4, 3, 2, false, true, 0>(p.E, A, B, out, count, p.C, N, K, s)
                 : run_pp<4, 2, 4, 2, false, true, 0>(p.E, A, B, out, count, p.C, N, K, s);

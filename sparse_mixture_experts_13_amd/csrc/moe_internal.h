@@ -71,7 +71,8 @@ hipError_t launch_expert_up_act(const Plan& p, const void* x_e, const int32_t* e
 // Backward token-row product out[e][m][n] = sum_k A[e][m][k] B[e][k][n] (A [C][K],
 // B [K][N], out [C][N] per expert; rows m < count[e]) on the ping-pong GEMM, times
 // act'(aux[e][m][n]) for grad_act 0 (ReLU) or 1 (GELU), plain for grad_act -1.
-// hipErrorNotSupported where that kernel does not apply (the caller falls back).
+// hipErrorNotSupported where that kernel does not apply (the caller falls back):
+// bf16 only, K >= 1024, capacity > 160 (> 64 when N >= 2048), 32-bit offsets.
 hipError_t launch_bwd_rows_pp(const Plan& p, const uint16_t* A, const uint16_t* B, uint16_t* out,
                               const uint16_t* aux, const int32_t* count, int N, int K, int grad_act,
                               hipStream_t s);
