@@ -146,6 +146,10 @@ TEST_WORKLOADS = {
     # N = 2048) on the ping-pong GEMM at a capacity below 161
     "mid_wide_bf16": Workload("mid_wide_bf16", T=600, d_model=1024, d_ff=2048, E=6, k=1,
                               capacity_factor=1.0, act="gelu", dtype="bf16"),
+    # d_ff = 2112: the last 512-row column tile of the up-projection and of the backward's
+    # dZ holds 64 rows, and the down-projection's contraction is 66 stages of 32
+    "wide_ragged_bf16": Workload("wide_ragged_bf16", T=700, d_model=2048, d_ff=2112, E=2, k=1,
+                                 capacity_factor=0.9, act="gelu", dtype="bf16"),
 }
 
 

@@ -29,6 +29,7 @@ CASES = [
     ("GLU up ring 256x256 (N=4096), down ping-pong 256x256", 1024, 2048, 40, 600, True),
     ("up and down ping-pong 128x512 (K=N=2048)", 2048, 2048, 40, 300, False),
     ("GLU up ping-pong 128x512 (K=N=2048), down ring 256x256 (K=1024)", 2048, 1024, 40, 300, True),
+    ("up and down ping-pong 128x512, N = 2112 (last column tile 64 rows), K = 2112", 2048, 2112, 40, 300, False),
 ]
 
 
