@@ -380,7 +380,20 @@ def cpu_baseline(wl, inputs, host_w1, host_w2, budget_s, min_s=10.0):
     desc = ("whole workload" if T == wl.T else f"first {T} of {wl.T} tokens routed as one batch") + \
         f", repeated {runs}x; float64 NumPy/OpenBLAS oracle: router, dispatch, gather, expert FFN, combine"
     return {"value": round(runs * T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": desc, "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+            "sample": desc, "seconds": round(dt, 2), "host_cpus": os.cpu_count(),
+            "cpu_model": host_cpu_model()}
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
