@@ -625,8 +625,13 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
   int lk = 0;
   auto issue_stage = [&](int slot) {
     unsigned char* base = smem + slot * STAGE;
-    const bf16_t* We = W + static_cast<int64_t>(lc.e) * N * K;
-    const bf16_t* Ae = A + static_cast<int64_t>(lc.e) * C * K;
+    // buffer loads into LDS: the expert's panels as buffer descriptors (raw, 32-bit
+    // data format), byte offsets per lane; the record counts bound every load to its
+    // panel (4-7% faster than the equivalent global loads into LDS)
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W + static_cast<int64_t>(lc.e) * N * K), (short)0, N * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(A + static_cast<int64_t>(lc.e) * C * K), (short)0, static_cast<int>(C * K * 2), 0x00020000);
 #pragma unroll
     for (int q = 0; q < WL; ++q) {
       const int p = (wave * WL + q) * 64 + lane;
@@ -642,7 +647,8 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
         if constexpr (GLU) wr = glu_row(wr, N >> 1);
         off = static_cast<uint32_t>(wr) * K + lk * BK + c * 8;
       }
-      __builtin_amdgcn_global_load_lds(We + off, (lds_void*)(base + (wave * WL + q) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void*)(base + (wave * WL + q) * 1024), 16,
+                                               static_cast<int>(off * 2), 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < AL; ++q) {
@@ -650,8 +656,8 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
       const int row = p / CPR;
       const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
       const uint32_t off = static_cast<uint32_t>(min(lc.mb * BM + row, lc.cnt - 1)) * K + lk * BK + c * 8;
-      __builtin_amdgcn_global_load_lds(Ae + off, (lds_void*)(base + BN * RB + (wave * AL + q) * 1024),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + BN * RB + (wave * AL + q) * 1024), 16,
+                                               static_cast<int>(off * 2), 0, 0, 0);
     }
   };
   // the loader cursor stops on the block's last stage: later issues re-read it
@@ -1231,9 +1237,10 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
   const int64_t lim = int64_t(1) << 32;
   if (int64_t(N) * K >= lim || p.C * K >= lim)
     return run_bf16<128, 128, 2, 2, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C > 160 && K >= 2048 && N >= 2048)
+  const bool pp_ok = int64_t(N) * K * 2 < (int64_t(1) << 31) && p.C * K * 2 < (int64_t(1) << 31);
+  if (pp_ok && p.C > 160 && K >= 2048 && N >= 2048)
     return run_pp<2, 4, 3, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C > 160 && K >= 2048) return run_pp<4, 2, 4, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (pp_ok && p.C > 160 && K >= 2048) return run_pp<4, 2, 4, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C > 160) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
     return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
@@ -1314,9 +1321,10 @@ hipError_t launch_expert_up_act(const Plan& p, const void* x_e, const int32_t* e
 hipError_t launch_bwd_rows_pp(const Plan& p, const bf16_t* A, const bf16_t* B, bf16_t* out,
                               const bf16_t* aux, const int32_t* count, int N, int K, int grad_act,
                               hipStream_t s) {
-  const int64_t lim = int64_t(1) << 32;
+  const int64_t lim = int64_t(1) << 31;  // byte offsets inside an expert's panels (buffer loads)
   const bool wide = N >= 2048;
-  if (p.dtype != 1 || K < 1024 || p.C <= (wide ? 64 : 160) || int64_t(N) * K >= lim || p.C * K >= lim)
+  if (p.dtype != 1 || K < 1024 || p.C <= (wide ? 64 : 160) || int64_t(N) * K * 2 >= lim ||
+      p.C * K * 2 >= lim)
     return hipErrorNotSupported;
   if (grad_act < 0)
     return wide ? run_pp<2, 4, 3, 2, false, true, 0>(p.E, A, B, out, count, p.C, N, K, s)
