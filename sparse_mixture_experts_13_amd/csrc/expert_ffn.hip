@@ -1051,7 +1051,30 @@ __global__ __launch_bounds__(512) void ffn_fused_bf16_kernel(
   }
 }
 
-// float32 grouped GEMM: 64 x 64 tile, 4 x 4 outputs per thread, BK = 16.
+// One 64-k stage of the float32 GEMM's two 64-row operand tiles, in registers.
+struct F32Stage {
+  float4 a[4], b[4];
+};
+
+template <bool GLU>
+__device__ __forceinline__ F32Stage f32_stage_load(const float* Ae, const float* We, int K, int k0,
+                                                   int tid, int rows, int n0, int N) {
+  F32Stage st;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + 256 * i, r = q >> 4, c = (q & 15) * 4;
+    st.a[i] = st.b[i] = float4{0.f, 0.f, 0.f, 0.f};
+    if (r < rows) st.a[i] = *reinterpret_cast<const float4*>(Ae + static_cast<int64_t>(r) * K + k0 + c);
+    const int wr = GLU ? glu_row(n0 + r, N >> 1) : n0 + r;
+    if (n0 + r < N) st.b[i] = *reinterpret_cast<const float4*>(We + static_cast<int64_t>(wr) * K + k0 + c);
+  }
+  return st;
+}
+
+// float32 grouped GEMM: 64 x 64 tile, 4 x 4 outputs per thread, 64-k steps loaded
+// with 16-byte vectors into registers one step ahead (the next step's loads are in
+// flight during this step's FMAs: small layers are latency-bound, a step of 16 k
+// with no prefetch paid a memory round trip each).
 template <int ACT, bool GLU>
 __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(const float* __restrict__ A,
                                                            const float* __restrict__ W,
@@ -1059,8 +1082,9 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(const float* __restri
                                                            const int32_t* __restrict__ count,
                                                            int64_t C, int N, int K, int n_mt,
                                                            int n_nt) {
-  __shared__ float sA[64][17];
-  __shared__ float sB[64][17];
+  constexpr int BK = 64, LDP = BK + 4;  // rows of 272 bytes: 16-byte aligned vector stores
+  __shared__ __align__(16) float sA[64][LDP];
+  __shared__ __align__(16) float sB[64][LDP];
   const int tid = threadIdx.x;
   int id = blockIdx.x;
   const int per_e = n_mt * n_nt;
@@ -1081,17 +1105,19 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32_kernel(const float* __restri
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  // thread q = tid + 256 i loads row q / 16, k chunk 4 (q % 16) of each operand
+  F32Stage st = f32_stage_load<GLU>(Ae, We, K, 0, tid, cnt - m0, n0, N);
+  for (int k0 = 0; k0 < K; k0 += BK) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i, r = q >> 4, c = q & 15;
-      sA[r][c] = m0 + r < cnt ? Ae[static_cast<int64_t>(r) * K + k0 + c] : 0.f;
-      const int wr = GLU ? glu_row(n0 + r, N >> 1) : n0 + r;
-      sB[r][c] = n0 + r < N ? We[static_cast<int64_t>(wr) * K + k0 + c] : 0.f;
+      const int q = tid + 256 * i, r = q >> 4, c = (q & 15) * 4;
+      *reinterpret_cast<float4*>(&sA[r][c]) = st.a[i];
+      *reinterpret_cast<float4*>(&sB[r][c]) = st.b[i];
     }
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
+    if (k0 + BK < K) st = f32_stage_load<GLU>(Ae, We, K, k0 + BK, tid, cnt - m0, n0, N);
+#pragma unroll 16
+    for (int kk = 0; kk < BK; ++kk) {
       float a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = sA[ty + 16 * i][kk];

@@ -452,14 +452,29 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 #pragma unroll
   for (int j = 0; j < NACC; ++j) acc[j] = 0.f;
   const int t = tid & 63, eg = tid >> 6;
+  constexpr int XL = 64 * FBK / 256, WL = Ecap * FBK / 256;  // loads per thread and stage
   for (int k0 = 0; k0 < d; k0 += FBK) {
-    for (int id = tid; id < 64 * FBK; id += 256) {
-      const int r = id / FBK, c = id - r * FBK;
-      sx[r * (FBK + 1) + c] = tok0 + r < T ? x[static_cast<int64_t>(tok0 + r) * d + k0 + c] : 0.f;
+    // every load of the stage in flight before the LDS stores (one memory round trip)
+    float xv[XL], wv[WL];
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int id = tid + 256 * i, r = id / FBK, c = id - r * FBK;
+      xv[i] = tok0 + r < T ? x[static_cast<int64_t>(tok0 + r) * d + k0 + c] : 0.f;
     }
-    for (int id = tid; id < Ecap * FBK; id += 256) {
-      const int r = id / FBK, c = id - r * FBK;
-      sw[r * (FBK + 1) + c] = r < E ? w_r[static_cast<int64_t>(r) * d + k0 + c] : 0.f;
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+      const int id = tid + 256 * i, r = id / FBK, c = id - r * FBK;
+      wv[i] = r < E ? w_r[static_cast<int64_t>(r) * d + k0 + c] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int id = tid + 256 * i, r = id / FBK, c = id - r * FBK;
+      sx[r * (FBK + 1) + c] = xv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+      const int id = tid + 256 * i, r = id / FBK, c = id - r * FBK;
+      sw[r * (FBK + 1) + c] = wv[i];
     }
     __syncthreads();
 #pragma unroll 4
