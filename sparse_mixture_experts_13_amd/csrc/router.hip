@@ -381,15 +381,16 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
         a[j][u] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
       }
     }
+    // unconditional: a wave past the last expert tile multiplies a copy of it (its
+    // fragments are read clamped) and drops the result at the write-out; a branch
+    // here moved every accumulator between AGPRs and VGPRs around each MFMA
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int u = 0; u < EW; ++u)
-        if (wave + 4 * u < n_et) {
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-            acc[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][u], bq[j][tt], acc[u][tt], 0, 0, 0);
-        }
+        for (int tt = 0; tt < TT; ++tt)
+          acc[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][u], bq[j][tt], acc[u][tt], 0, 0, 0);
   }
   __syncthreads();  // ring reads done before the logits tile overwrites it
 
