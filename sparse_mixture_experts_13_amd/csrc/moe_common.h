@@ -128,15 +128,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
 // Inclusive prefix sum over the 64 lanes.
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 #pragma unroll

@@ -49,79 +49,6 @@ __device__ __forceinline__ int key_expert(uint64_t key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
 }
 
-// Rank the tokens of one block.  lg: logits [64][ld] in LDS (bias not yet added).
-// Wave w handles tokens w, w+4, ...; lane l holds experts l, l+64, ...
-// psum (may be null): the block's row of per-expert probability sums; red:
-// [4][ldh] floats of LDS for the cross-wave sum, free once ranking is done.
-__device__ void topk_epilogue(const float* lg, int ld, int tok0, int ntok, int E, int k,
-                              const float* __restrict__ bias, int32_t* __restrict__ expert_idx,
-                              float* __restrict__ gate, int* hl, int ldh, int wave, int lane,
-                              float* __restrict__ psum, float* red, float* __restrict__ hout,
-                              int ldo) {
-  const int nper = (E + kWave - 1) / kWave;  // <= 8
-  float pacc[kMaxE / kWave];
-#pragma unroll
-  for (int i = 0; i < kMaxE / kWave; ++i) pacc[i] = 0.f;
-  for (int t = wave; t < ntok; t += 4) {
-    const float* row = lg + t * ld;
-    float hv[kMaxE / kWave];
-    uint64_t kv[kMaxE / kWave];
-#pragma unroll
-    for (int i = 0; i < kMaxE / kWave; ++i) {
-      hv[i] = -INFINITY;
-      kv[i] = 0;
-      const int e = lane + kWave * i;
-      if (i < nper && e < E) {
-        float h = row[e];
-        if (bias) h = h + bias[e];  // one float32 rounding after the full dot product
-        hv[i] = h;
-        kv[i] = make_key(h, e);
-        if (hout) hout[static_cast<int64_t>(tok0 + t) * ldo + e] = h;
-      }
-    }
-    uint64_t best0 = 0, bestc = 0;
-    for (int c = 0; c < k; ++c) {
-      uint64_t m = 0;
-#pragma unroll
-      for (int i = 0; i < kMaxE / kWave; ++i) m = kv[i] > m ? kv[i] : m;
-      m = wave_max_u64(m);
-#pragma unroll
-      for (int i = 0; i < kMaxE / kWave; ++i)
-        if (kv[i] == m) kv[i] = 0;  // keys are unique: removes exactly the winner
-      if (c == 0) best0 = m;
-      if (lane == c) bestc = m;
-    }
-    const float hmax = key_logit(best0);
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxE / kWave; ++i) s += expf(hv[i] - hmax);  // exp(-inf) = 0
-    s = wave_sum(s);
-    if (lane < k) {
-      const int e = key_expert(bestc);
-      const float p = expf(key_logit(bestc) - hmax) / s;
-      const int64_t o = static_cast<int64_t>(tok0 + t) * k + lane;
-      expert_idx[o] = e;
-      gate[o] = p;
-      atomicAdd(&hl[lane * ldh + e], 1);
-    }
-    if (psum) {
-#pragma unroll
-      for (int i = 0; i < kMaxE / kWave; ++i) pacc[i] += expf(hv[i] - hmax) / s;
-    }
-  }
-  if (psum) {
-    __syncthreads();  // every wave is done with the logits tile that red overlays
-#pragma unroll
-    for (int i = 0; i < kMaxE / kWave; ++i) {
-      const int e = lane + kWave * i;
-      if (i < nper && e < ldh) red[wave * ldh + e] = pacc[i];
-    }
-    __syncthreads();
-    for (int e = wave * kWave + lane; e < E; e += 4 * kWave)
-      psum[e] = ((red[e] + red[ldh + e]) + red[2 * ldh + e]) + red[3 * ldh + e];
-  }
-}
-
 __device__ __forceinline__ void write_hist(const int* hl, int ldh, int E, int k, int NB, int b,
                                            int* __restrict__ hist, int tid, int nthreads) {
   for (int i = tid; i < E * k; i += nthreads) {
@@ -196,9 +123,9 @@ __host__ __device__ inline int64_t router_lg_bytes(int TB, int Epad) {
   return static_cast<int64_t>(TB) * (Epad + 4) * 4;
 }
 
-// Rank the tokens of a block from the logits tile lg [TB][ld] in LDS.  Sixteen
-// lanes share a token (a wave ranks four tokens at a time); lane `sub` holds
-// experts sub, sub+16, ...  Keys order by (logit desc, expert asc).
+// Rank the tokens of a block from the logits tile lg [TB][ld] in LDS (both
+// routers).  Sixteen lanes share a token (a wave ranks four tokens at a time);
+// lane `sub` holds experts sub, sub+16, ...  Keys order by (logit desc, expert asc).
 template <int NV>
 __device__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int ntok, int E, int k,
                                 const float* __restrict__ bias, int32_t* __restrict__ expert_idx,
@@ -206,9 +133,14 @@ __device__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int n
                                 float* __restrict__ psum, float* red, float* __restrict__ hout,
                                 int ldo) {
   const int grp = lane >> 4, sub = lane & 15;
-  float pacc[NV];
+  float pacc[NV], bv[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) pacc[i] = 0.f;
+  for (int i = 0; i < NV; ++i) {
+    pacc[i] = 0.f;
+    // the lane's bias values once: a global load in the token loop made every
+    // round wait for the previous round's stores (loads and stores share vmcnt)
+    bv[i] = bias && sub + 16 * i < E ? bias[sub + 16 * i] : 0.f;
+  }
   for (int base = 0; base < TB; base += 16) {
     const int t = base + wave * 4 + grp;
     const bool valid = t < ntok;
@@ -219,7 +151,7 @@ __device__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int n
       hv[i] = -INFINITY;
       if (valid && e < E) {
         float h = lg[t * ld + e];
-        if (bias) h = h + bias[e];  // one float32 rounding after the full dot product
+        if (bias) h = h + bv[i];  // one float32 rounding after the full dot product
         hv[i] = h;
         if (hout) hout[static_cast<int64_t>(tok0 + t) * ldo + e] = h;
       }
@@ -422,8 +354,9 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// float32 router (float32 token dtype): float32 FMA dot products.
-// NACC = experts per thread; the block covers Ecap = 4 * NACC >= E experts.
+// float32 router (float32 token dtype): float32 FMA dot products, 64 tokens per
+// block, then the shared ranking epilogue.  NACC = experts per thread; the block
+// covers Ecap = 4 * NACC >= E experts.
 // ---------------------------------------------------------------------------
 constexpr int FBK = 32;
 __host__ __device__ inline int64_t router_f32_stage_bytes(int Ecap) {
@@ -490,8 +423,8 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 #pragma unroll
   for (int j = 0; j < NACC; ++j) lg[t * ld + eg + 4 * j] = acc[j];
   __syncthreads();
-  topk_epilogue(lg, ld, tok0, ntok, E, k, bias, expert_idx, gate, hl, Ecap, wave, lane,
-                psum ? psum + static_cast<int64_t>(b) * ldp : nullptr, lg, hout, ldp);
+  topk_epilogue16<NACC / 4>(lg, ld, 64, tok0, ntok, E, k, bias, expert_idx, gate, hl, Ecap, wave,
+                            lane, psum ? psum + static_cast<int64_t>(b) * ldp : nullptr, lg, hout, ldp);
   __syncthreads();
   write_hist(hl, Ecap, E, k, NB, b, hist, tid, 256);
 }
