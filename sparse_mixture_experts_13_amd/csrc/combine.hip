@@ -11,7 +11,7 @@
 
 namespace moe {
 
-template <typename T>
+template <typename T, int CH>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_e,
                                                       const int32_t* __restrict__ expert_idx,
                                                       const int32_t* __restrict__ slot,
@@ -21,53 +21,86 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_e,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= ntok) return;
-  // served choices in choice order; fully unrolled so the arrays stay in registers
+  // served choices in choice order: lane c loads choice c (one memory round trip
+  // for all of them), readlane hands each to the whole wave; fully unrolled so the
+  // arrays stay in registers
+  int sl = -1, el = -1;
+  float gl = 0.f;
+  if (lane < k) {
+    const int64_t o = static_cast<int64_t>(t) * k + lane;
+    sl = slot[o];
+    el = expert_idx[o];
+    gl = gate[o];
+  }
   int64_t off[kMaxK];
   float g[kMaxK];
 #pragma unroll
   for (int c = 0; c < kMaxK; ++c) {
-    off[c] = -1;
-    g[c] = 0.f;
-    if (c < k) {
-      const int64_t o = static_cast<int64_t>(t) * k + c;
-      const int s = slot[o];
-      const int e = expert_idx[o];
-      if (s >= 0 && s < C && e >= 0 && e < E) {
-        off[c] = (e * C + s) * d;
-        g[c] = gate[o];
-      }
-    }
+    const int s = __builtin_amdgcn_readlane(sl, c);
+    const int e = __builtin_amdgcn_readlane(el, c);
+    const bool ok = c < k && s >= 0 && s < C && e >= 0 && e < E;
+    off[c] = ok ? (e * C + s) * d : -1;
+    g[c] = ok ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gl), c)) : 0.f;
   }
   T* dst = y + static_cast<int64_t>(t) * d;
-  for (int64_t v = lane; v < d / 8; v += kWave) {
-    float acc[8];
+  // CH 8-element chunks per lane: the loads of a choice issue together (a lane
+  // past the row end reads the last chunk again and stores nothing), all stores
+  // after all loads (a load issued after a store also waits for that store:
+  // loads and stores share vmcnt); per element the choices add in choice order
+  const int64_t nch = d / 8;
+  for (int64_t v0 = lane; v0 < nch; v0 += kWave * CH) {
+    float acc[CH][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
 #pragma unroll
     for (int c = 0; c < kMaxK; ++c) {
       if (off[c] >= 0) {
-        float r[8];
-        vec8<T>::load(y_e + off[c] + v * 8, r);
+        float r[CH][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[c], r[i], acc[i]);
+        for (int j = 0; j < CH; ++j) {
+          const int64_t v = min(v0 + j * kWave, nch - 1);
+          vec8<T>::load(y_e + off[c] + v * 8, r[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[j][i] = fmaf(g[c], r[j][i], acc[j][i]);
       }
     }
-    vec8<T>::store(dst + v * 8, acc);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int64_t v = v0 + j * kWave;
+      if (v < nch) vec8<T>::store(dst + v * 8, acc[j]);
+    }
   }
+}
+
+template <typename T, int CH>
+static void run_combine(const Plan& p, const void* y_e, const int32_t* expert_idx,
+                        const int32_t* slot, const float* gate, void* y, hipStream_t s) {
+  const int nblk = static_cast<int>((p.T + 3) / 4);
+  hipLaunchKernelGGL((combine_kernel<T, CH>), dim3(nblk), dim3(256), 0, s,
+                     static_cast<const T*>(y_e), expert_idx, slot, gate, static_cast<int>(p.T), p.E,
+                     p.k, p.C, p.d, static_cast<T*>(y));
+}
+
+template <typename T>
+static void run_combine_typed(const Plan& p, const void* y_e, const int32_t* expert_idx,
+                              const int32_t* slot, const float* gate, void* y, hipStream_t s) {
+  // chunks per lane: enough for the row in one pass up to 256 chunks (2048 elements)
+  const int64_t per_lane = (p.d / 8 + kWave - 1) / kWave;
+  if (per_lane <= 1) run_combine<T, 1>(p, y_e, expert_idx, slot, gate, y, s);
+  else if (per_lane <= 2) run_combine<T, 2>(p, y_e, expert_idx, slot, gate, y, s);
+  else run_combine<T, 4>(p, y_e, expert_idx, slot, gate, y, s);
 }
 
 hipError_t launch_combine(const Plan& p, const void* y_e, const int32_t* expert_idx,
                           const int32_t* slot, const float* gate, void* y, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  const int nblk = static_cast<int>((p.T + 3) / 4);
-  if (p.dtype == 1)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(nblk), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(y_e), expert_idx, slot, gate,
-                       static_cast<int>(p.T), p.E, p.k, p.C, p.d, static_cast<bf16_t*>(y));
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(nblk), dim3(256), 0, s,
-                       static_cast<const float*>(y_e), expert_idx, slot, gate,
-                       static_cast<int>(p.T), p.E, p.k, p.C, p.d, static_cast<float*>(y));
+  if (p.dtype == 1) run_combine_typed<bf16_t>(p, y_e, expert_idx, slot, gate, y, s);
+  else run_combine_typed<float>(p, y_e, expert_idx, slot, gate, y, s);
   return hipGetLastError();
 }
 

@@ -73,6 +73,7 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(const int* __restric
 // Phase 3: 16 tokens per 256-thread block (TB / 16 blocks share one router
 // block of TB tokens).
 constexpr int kSlotTokens = 16;
+constexpr int kGatherBatch = 8;  // 16-byte vectors per thread per copy batch
 
 __global__ __launch_bounds__(256) void dispatch_slot_gather_kernel(
     const uint8_t* __restrict__ x, const int32_t* __restrict__ expert_idx, int T, int E, int k,
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(256) void dispatch_slot_gather_kernel(
   __shared__ int sidx[kMaxRouterBlock * kMaxK];
   __shared__ int dst_e[kSlotTokens * kMaxK];
   __shared__ int dst_s[kSlotTokens * kMaxK];
+  __shared__ bool served[kSlotTokens];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kSlotTokens;
   const int b = t0 / TB;
@@ -111,22 +113,38 @@ __global__ __launch_bounds__(256) void dispatch_slot_gather_kernel(
     dst_s[tl * k + c] = s;
   }
   __syncthreads();
-  const int64_t nvec = row_bytes / 16;
-  for (int tl = wave; tl < kSlotTokens; tl += 4) {
-    const int t = t0 + tl;
-    if (t >= T) break;
+  if (tid < kSlotTokens) {
     bool any = false;
-    for (int c = 0; c < k; ++c) any |= dst_s[tl * k + c] >= 0;
-    if (!any) continue;
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(t) * row_bytes);
-    for (int64_t v = lane; v < nvec; v += kWave) {
-      const u32x4 val = src[v];
-      for (int c = 0; c < k; ++c) {
-        const int s = dst_s[tl * k + c];
-        if (s >= 0) {
-          const int e = dst_e[tl * k + c];
-          u32x4* dst = reinterpret_cast<u32x4*>(x_e + (e * C + s) * row_bytes);
-          dst[v] = val;
+    for (int c = 0; c < k; ++c) any |= dst_s[tid * k + c] >= 0;
+    served[tid] = any;
+  }
+  __syncthreads();
+  // copy: the group's rows as one flat list of 16-byte vectors over all threads,
+  // kGatherBatch loads per thread in flight before their stores (loads and stores
+  // share vmcnt, so a load issued after a store waits for that store as well)
+  const int nvec = static_cast<int>(row_bytes / 16);
+  const int items = (tend - t0) * nvec;
+  for (int base = 0; base < items; base += 256 * kGatherBatch) {
+    u32x4 val[kGatherBatch];
+#pragma unroll
+    for (int j = 0; j < kGatherBatch; ++j) {
+      const int it = base + j * 256 + tid;
+      const int tl = it / nvec, v = it - tl * nvec;
+      if (it < items && served[tl])
+        val[j] = reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(t0 + tl) * row_bytes)[v];
+    }
+    wait_vmcnt<0>();  // one wait for the batch: none between the stores below
+#pragma unroll
+    for (int j = 0; j < kGatherBatch; ++j) {
+      const int it = base + j * 256 + tid;
+      const int tl = it / nvec, v = it - tl * nvec;
+      if (it < items && served[tl]) {
+        for (int c = 0; c < k; ++c) {
+          const int sl = dst_s[tl * k + c];
+          if (sl >= 0) {
+            const int e = dst_e[tl * k + c];
+            reinterpret_cast<u32x4*>(x_e + (e * C + sl) * row_bytes)[v] = val[j];
+          }
         }
       }
     }
