@@ -828,29 +828,27 @@ namespace moe {
 
 constexpr int kClipBlocks = 512;
 
-// Sum of squares of one array in float64.  Block b takes the b-th contiguous
-// range of its 8-element vectors (16-byte loads, four vectors in flight per
-// thread, four float64 accumulators per thread in a fixed assignment); the last
-// block also takes the n % 8 tail.  Deterministic: a fixed order throughout.
+// Sum of squares of one array in float64.  Block b (512 threads) takes the b-th
+// contiguous range of its 8-element vectors: full batches of eight 16-byte
+// loads per thread issued together (enough bytes in flight to keep HBM busy),
+// then the range's remainder one vector per thread; four float64 accumulators
+// per thread in a fixed assignment; the last block also takes the n % 8 tail.
+// Deterministic: a fixed order throughout.
+constexpr int kSumsqThreads = 512;
+
 template <typename T>
-__global__ __launch_bounds__(256) void clip_sumsq_kernel(const T* __restrict__ p, int64_t n,
-                                                         double* __restrict__ part) {
-  constexpr int U = 4;
-  __shared__ double red[256];
+__global__ __launch_bounds__(kSumsqThreads) void clip_sumsq_kernel(const T* __restrict__ p, int64_t n,
+                                                                   double* __restrict__ part) {
+  constexpr int U = 8, NT = kSumsqThreads;
+  __shared__ double red[NT];
   const int64_t n8 = n >> 3;
   const int64_t b0 = n8 * blockIdx.x / gridDim.x, b1 = n8 * (blockIdx.x + 1) / gridDim.x;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int64_t i = b0 + threadIdx.x; i < b1; i += 256 * U) {
+  int64_t i = b0 + threadIdx.x;
+  for (; i + NT * (U - 1) < b1; i += NT * U) {
     float v[U][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = i + 256 * u;
-      if (j < b1) vec8<T>::load(p + 8 * j, v[u]);
-      else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
-      }
-    }
+    for (int u = 0; u < U; ++u) vec8<T>::load(p + 8 * (i + NT * u), v[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -859,14 +857,23 @@ __global__ __launch_bounds__(256) void clip_sumsq_kernel(const T* __restrict__ p
         acc[e & 3] = fma(x, x, acc[e & 3]);
       }
   }
+  for (; i < b1; i += NT) {
+    float v[8];
+    vec8<T>::load(p + 8 * i, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double x = static_cast<double>(v[e]);
+      acc[e & 3] = fma(x, x, acc[e & 3]);
+    }
+  }
   if (blockIdx.x == gridDim.x - 1)
-    for (int64_t i = 8 * n8 + threadIdx.x; i < n; i += 256) {
-      const double x = static_cast<double>(ld_f32(p + i));
+    for (int64_t j = 8 * n8 + threadIdx.x; j < n; j += NT) {
+      const double x = static_cast<double>(ld_f32(p + j));
       acc[0] = fma(x, x, acc[0]);
     }
   red[threadIdx.x] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = NT / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
@@ -898,31 +905,48 @@ __global__ __launch_bounds__(256) void clip_coef_kernel(const double* __restrict
   }
 }
 
-// p *= coef in place, 8-element vectors (two in flight per thread), the n % 8
-// tail by block 0.  coef == 1 leaves every value as it is (x * 1 rounds to x),
-// so the pass then reads and writes nothing.
+// p *= coef in place.  Block b scales vectors [b, b + 1) * 256 * kScaleVecs of 8
+// elements, each thread kScaleVecs of them (all loads before the stores, one pass
+// per thread: a load issued after a store would also wait for that store); the
+// n % 8 tail by block 0.  coef == 1 leaves every value as it is (x * 1 rounds to
+// x), so the pass then reads and writes nothing.
+constexpr int kScaleVecs = 4;
+
 template <typename T>
 __global__ __launch_bounds__(256) void clip_scale_kernel(T* __restrict__ p, int64_t n,
                                                          const float* __restrict__ nc) {
-  constexpr int U = 2;
+  constexpr int U = kScaleVecs;
   const float c = nc[1];
   if (c == 1.0f) return;
-  const int64_t n8 = n >> 3, S = static_cast<int64_t>(gridDim.x) * 256;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8; i += S * U) {
-    float v[U][8];
+  const int64_t n8 = n >> 3;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 * U + threadIdx.x;
+  float v[U][8];
+  if (i + 256 * (U - 1) < n8) {
 #pragma unroll
+    for (int u = 0; u < U; ++u) vec8<T>::load(p + 8 * (i + 256 * u), v[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[u][e] *= c;
+      vec8<T>::store(p + 8 * (i + 256 * u), v[u]);
+    }
+  } else {
     for (int u = 0; u < U; ++u)
-      if (i + u * S < n8) vec8<T>::load(p + 8 * (i + u * S), v[u]);
+      if (i + 256 * u < n8) {
+        vec8<T>::load(p + 8 * (i + 256 * u), v[0]);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (i + u * S < n8) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[u][e] *= c;
-        vec8<T>::store(p + 8 * (i + u * S), v[u]);
+        for (int e = 0; e < 8; ++e) v[0][e] *= c;
+        vec8<T>::store(p + 8 * (i + 256 * u), v[0]);
       }
   }
   if (blockIdx.x == 0)
-    for (int64_t i = 8 * n8 + threadIdx.x; i < n; i += 256) st_f32(p + i, ld_f32(p + i) * c);
+    for (int64_t j = 8 * n8 + threadIdx.x; j < n; j += 256) st_f32(p + j, ld_f32(p + j) * c);
+}
+
+// blocks of clip_scale_kernel for an n-element array (at least one: block 0 takes the tail)
+inline unsigned clip_scale_blocks(int64_t n) {
+  const int64_t per = 256LL * kScaleVecs;
+  return static_cast<unsigned>(std::max<int64_t>(1, ((n >> 3) + per - 1) / per));
 }
 
 template <typename T>
@@ -931,19 +955,16 @@ static hipError_t clip_typed(const Plan& p, float* dw_r, float* dbias, T* dw1, T
   const int64_t nw = int64_t(p.E) * p.d * p.f, nw1 = int64_t(p.E) * p.d * p.w1_rows();
   const int64_t nr = dw_r ? int64_t(p.E) * p.d : 0, nb = dbias ? p.E : 0;
   // empty arrays still write their (zero) partials
-  hipLaunchKernelGGL(clip_sumsq_kernel<float>, dim3(kClipBlocks), dim3(256), 0, s, dw_r, nr, part);
-  hipLaunchKernelGGL(clip_sumsq_kernel<float>, dim3(kClipBlocks), dim3(256), 0, s, dbias, nb,
-                     part + kClipBlocks);
-  hipLaunchKernelGGL(clip_sumsq_kernel<T>, dim3(kClipBlocks), dim3(256), 0, s, dw1, nw1,
-                     part + 2 * kClipBlocks);
-  hipLaunchKernelGGL(clip_sumsq_kernel<T>, dim3(kClipBlocks), dim3(256), 0, s, dw2, nw,
-                     part + 3 * kClipBlocks);
+  const dim3 sb(kSumsqThreads);
+  hipLaunchKernelGGL(clip_sumsq_kernel<float>, dim3(kClipBlocks), sb, 0, s, dw_r, nr, part);
+  hipLaunchKernelGGL(clip_sumsq_kernel<float>, dim3(kClipBlocks), sb, 0, s, dbias, nb, part + kClipBlocks);
+  hipLaunchKernelGGL(clip_sumsq_kernel<T>, dim3(kClipBlocks), sb, 0, s, dw1, nw1, part + 2 * kClipBlocks);
+  hipLaunchKernelGGL(clip_sumsq_kernel<T>, dim3(kClipBlocks), sb, 0, s, dw2, nw, part + 3 * kClipBlocks);
   hipLaunchKernelGGL(clip_coef_kernel, dim3(1), dim3(256), 0, s, part, p.E, max_norm, nc);
-  const unsigned g = 2048;
-  if (nr) hipLaunchKernelGGL(clip_scale_kernel<float>, dim3(g), dim3(256), 0, s, dw_r, nr, nc);
-  if (nb) hipLaunchKernelGGL(clip_scale_kernel<float>, dim3(1), dim3(256), 0, s, dbias, nb, nc);
-  hipLaunchKernelGGL(clip_scale_kernel<T>, dim3(g), dim3(256), 0, s, dw1, nw1, nc);
-  hipLaunchKernelGGL(clip_scale_kernel<T>, dim3(g), dim3(256), 0, s, dw2, nw, nc);
+  if (nr) hipLaunchKernelGGL(clip_scale_kernel<float>, dim3(clip_scale_blocks(nr)), dim3(256), 0, s, dw_r, nr, nc);
+  if (nb) hipLaunchKernelGGL(clip_scale_kernel<float>, dim3(clip_scale_blocks(nb)), dim3(256), 0, s, dbias, nb, nc);
+  hipLaunchKernelGGL(clip_scale_kernel<T>, dim3(clip_scale_blocks(nw1)), dim3(256), 0, s, dw1, nw1, nc);
+  hipLaunchKernelGGL(clip_scale_kernel<T>, dim3(clip_scale_blocks(nw)), dim3(256), 0, s, dw2, nw, nc);
   return hipGetLastError();
 }
 
