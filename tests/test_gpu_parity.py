@@ -372,6 +372,28 @@ def test_f32_gelu_top2():
     _run_case(wl, W.make_inputs(wl), "f32 top-2 gelu")
 
 
+# float32 router blocks cover 32, 64, 128, 256 or 512 experts (2 to 32 ranking keys per
+# lane); the Zipf cases add the per-expert logit bias
+F32_WIDE = [(60, 2, 0.0), (100, 3, 1.1), (250, 8, 0.0), (512, 8, 1.1)]
+
+
+@pytest.mark.parametrize("E,k,zipf", F32_WIDE,
+                         ids=[f"E{e}-k{k}" + ("-zipf" if z else "") for e, k, z in F32_WIDE])
+def test_f32_many_experts(E, k, zipf):
+    """float32 layers at every router block width: the layer against the oracle, and the
+    load-balancing loss (the ranking epilogue's probability sums) with identical repeats."""
+    wl = BASE.replace(T=257, d_model=64, d_ff=64, E=E, k=k, capacity_factor=4.0, act="relu",
+                      dtype="f32", zipf_s=zipf)
+    label = f"f32 E={E} k={k} zipf={zipf}"
+    inputs = W.make_inputs(wl)
+    _run_case(wl, inputs, label)
+    dev = Dev(wl, inputs)
+    idx, gate, aux = dev.run_router_aux(alpha=1e-2)
+    check_router_aux(wl, inputs, idx, gate, aux, 1e-2, label)
+    _, _, aux2 = dev.run_router_aux(alpha=1e-2)
+    np.testing.assert_array_equal(aux, aux2)
+
+
 def test_rre_invalid_group_ids():
     wl = W.TEST_WORKLOADS["rre_small_bf16"].replace(T=200)
     inputs = W.make_inputs(wl)
