@@ -402,9 +402,15 @@ __global__ __launch_bounds__(256) void bgemm_kernel(
       const int q = it * 256 + tid;
       const int ml = q / CPRow, c = q % CPRow;
       const int m = m0 + ml, n = n0 + c * 8;
-      if (m < Mv && n < N)
-        *reinterpret_cast<u32x4*>(Op + static_cast<int64_t>(m) * ldo + n) =
-            *reinterpret_cast<const u32x4*>(st + ml * OP + c * 8);
+      if (m < Mv && n < N) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + ml * OP + c * 8);
+        u32x4* dst = reinterpret_cast<u32x4*>(Op + static_cast<int64_t>(m) * ldo + n);
+        // both operands contracted over their leading (token) dimension: the weight
+        // gradients, a write stream the backward does not read again; non-temporal
+        // stores keep it from allocating in L2 (Switch-Base backward 829 -> 752 us)
+        if constexpr (!AKC && !BKC) __builtin_nontemporal_store(v, dst);
+        else *dst = v;
+      }
     }
   }
 }
