@@ -11,6 +11,20 @@
 
 namespace moe {
 
+// Eight output values with non-temporal stores: y is the layer's result, not read
+// again here, and at these sizes it does not stay in L2 for the next reader anyway
+// (Switch-Base combine 9.7 -> 9.0 us, step 0.2992 -> 0.2980 ms).
+__device__ __forceinline__ void store8_nt(bf16_t* p, const float* v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store8_nt(float* p, const float* v) {
+  __builtin_nontemporal_store(floatx4{v[0], v[1], v[2], v[3]}, reinterpret_cast<floatx4*>(p));
+  __builtin_nontemporal_store(floatx4{v[4], v[5], v[6], v[7]}, reinterpret_cast<floatx4*>(p + 4));
+}
+
 template <typename T, int CH>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_e,
                                                       const int32_t* __restrict__ expert_idx,
@@ -72,7 +86,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_e,
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int64_t v = v0 + j * kWave;
-      if (v < nch) vec8<T>::store(dst + v * 8, acc[j]);
+      if (v < nch) store8_nt(dst + v * 8, acc[j]);
     }
   }
 }
