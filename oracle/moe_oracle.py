@@ -26,8 +26,11 @@ Where the pages leave a step open, the reading taken is stated at the function.
 
 Pinned by tests/test_oracle_*.py against closed forms, brute force, a second
 formulation (one-hot dispatch/combine tensors), hand-worked fixtures in
-tests/golden/ and the published SplitMix64 outputs.  Every function here has a
-pin; none is "parity unpinned".
+tests/golden/ and the published SplitMix64 outputs.  The sampled-token path used
+at full layer size (``forward_rows``, ``route_and_dispatch``) is pinned against
+the dense one-hot formulation and a brute-force top-k on small layers with drops,
+two served choices, a Zipf bias, GLU experts and invalid RRE groups.  Every
+function here has a pin; none is "parity unpinned".
 
 Array conventions: bf16 tensors are np.uint16 raw bit patterns, fp32 tensors
 np.float32 (see ``as_f64``).

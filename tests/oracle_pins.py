@@ -341,6 +341,96 @@ def check_dense_equals_sparse(rng):
             np.testing.assert_allclose(r["y"], dense_layer(wl, inp, r), rtol=1e-12, atol=1e-12)
 
 
+def _rows_cases(rng):
+    """Small layers for the sampled-token path: top-1 with drops, top-2 whose second
+    choices overflow, a Zipf bias, GLU experts, and RRE with invalid group ids."""
+    cases = []
+    wl, inp = _rand_layer(rng, 96, 16, 24, 4, 1, 0.75, "relu")
+    cases.append(("top1_drops", wl, inp))
+    wl, inp = _rand_layer(rng, 80, 8, 12, 5, 2, 1.0, "gelu")
+    cases.append(("top2_second_choice_drops", wl, inp))
+    wl, inp = _rand_layer(rng, 64, 16, 8, 6, 2, 0.8, "gelu", zipf=True)
+    cases.append(("top2_zipf", wl, inp))
+    wl, inp = _rand_layer(rng, 70, 8, 12, 4, 2, 1.25, "relu", glu=True)
+    cases.append(("top2_glu", wl, inp))
+    T, G, E = 90, 3, 6
+    wl, inp = _rand_layer(rng, T, 8, 12, E, 1, 1.0, "gelu")
+    wl.route, wl.n_groups, wl.rre_seed = "rre", G, 99
+    gid = rng.integers(0, G, size=T).astype(np.int32)
+    gid[[3, 17, 40]] = [-1, G, 7]
+    inp["group_id"], inp["w_r"], inp["bias"] = gid, None, None
+    cases.append(("rre_invalid_groups", wl, inp))
+    return cases
+
+
+def check_forward_rows(rng):
+    """forward_rows (one token at a time) against the dense one-hot formulation of the
+    whole layer and against forward's y, on rows that include dropped tokens and tokens
+    with both choices served (Switch notes 2.1 Eq. 2, 2.2 dropping)."""
+    for name, wl, inp in _rand_cases_checked(rng):
+        r = O.forward(wl, inp)
+        served = (r["slot"] >= 0).sum(axis=1)
+        T = wl.T
+        rows = [0, T - 1]
+        rows += list(np.nonzero(served == 0)[0][:4])
+        rows += list(np.nonzero(served >= 2)[0][:4])
+        rows += list(np.nonzero((served == 1) & (r["slot"][:, 0] < 0))[0][:4])
+        rows += list(rng.choice(T, size=6, replace=False))
+        rows = np.array(sorted(set(int(t) for t in rows)))
+        w1, w2 = inp["w1"], inp["w2"]
+        got = O.forward_rows(wl, inp, rows, lambda e: (w1[e], w2[e]))
+        np.testing.assert_allclose(got, dense_layer(wl, inp, r)[rows], rtol=1e-12, atol=1e-12,
+                                   err_msg=name)
+        np.testing.assert_allclose(got, r["y"][rows], rtol=1e-12, atol=1e-12, err_msg=name)
+        assert (got[served[rows] == 0] == 0).all(), name
+
+
+def _rand_cases_checked(rng):
+    """The cases of ``_rows_cases`` after checking that each exercises what it names."""
+    cases = _rows_cases(rng)
+    for name, wl, inp in cases:
+        r = O.forward(wl, inp)
+        if "drops" in name or name == "top2_zipf":
+            assert (r["slot"] < 0).any(), name
+        if name == "top2_second_choice_drops":
+            assert ((r["slot"][:, 0] >= 0) & (r["slot"][:, 1] < 0)).any(), name
+            assert ((r["slot"] >= 0).sum(axis=1) == 2).any(), name
+        if name == "rre_invalid_groups":
+            assert (r["expert_idx"][:, 0] < 0).sum() == 3, name
+    return cases
+
+
+def check_route_and_dispatch(rng):
+    """route_and_dispatch (routing for the sampled-token path) against the routing that
+    forward returns, the one-hot dispatch formulation and a brute-force top-k
+    (Switch notes 2.1 and 2.2)."""
+    for name, wl, inp in _rows_cases(rng):
+        rd = O.route_and_dispatch(wl, inp)
+        r = O.forward(wl, inp)
+        for key in ("expert_idx", "slot", "expert_count", "slot_token"):
+            np.testing.assert_array_equal(rd[key], r[key], err_msg=f"{name}: {key}")
+        np.testing.assert_array_equal(rd["gate"], r["gate"], err_msg=name)
+        assert rd["capacity"] == r["capacity"]
+        C = math.ceil(Fraction(wl.k * wl.T) * Fraction(wl.capacity_factor) / wl.E)
+        assert rd["capacity"] == C, name
+        _, slot2 = onehot_dispatch(rd["expert_idx"], wl.E, C)
+        np.testing.assert_array_equal(rd["slot"], slot2, err_msg=name)
+        if wl.route == "topk":
+            # the logits themselves are pinned by the exact-arithmetic checks above; rank
+            # those by brute force (value desc, index asc) and form the softmax in float64
+            h = np.asarray(rd["logits"], np.float64)
+            h_exact = O.as_f64(inp["x"]) @ O.as_f64(inp["w_r"]).T
+            if inp["bias"] is not None:
+                h_exact = h_exact + O.as_f64(inp["bias"])
+            np.testing.assert_allclose(h, h_exact, rtol=1e-6, atol=1e-6, err_msg=name)
+            for t in range(wl.T):
+                order = sorted(range(wl.E), key=lambda e: (-h[t, e], e))
+                assert list(rd["expert_idx"][t]) == order[:wl.k], name
+                p = np.exp(h[t] - h[t].max())
+                p /= p.sum()
+                np.testing.assert_allclose(rd["gate"][t], p[order[:wl.k]], rtol=1e-6, err_msg=name)
+
+
 def check_glu_coordinate_gate(rng):
     """GLU FFN (MosaicBERT review, methodology) reduced to the plain FFN: with every V
     row a multiple a_j of the unit vector of input coordinate i, unit j's gate is

@@ -169,6 +169,34 @@ def _backward_glu_variant(mode):
     return bwd
 
 
+def _forward_rows_variant(mode):
+    """forward_rows with one planted mistake: the second choice skipped, or the
+    first choice's gate used for every choice (test code only)."""
+    def rows_fn(wl, inputs, rows, weights, routing=None):
+        if routing is None:
+            routing = O.route_and_dispatch(wl, inputs)
+        out = np.zeros((len(rows), wl.d_model))
+        for i, t in enumerate(rows):
+            for c in range(wl.k):
+                s = int(routing["slot"][t, c])
+                if s < 0 or (mode == "first_choice_only" and c >= 1):
+                    continue
+                e = int(routing["expert_idx"][t, c])
+                w1_e, w2_e = weights(e)
+                ye = O.expert_apply(O.as_f64(inputs["x"][t:t + 1]), w1_e, w2_e, wl.act, O.is_glu(wl))[0]
+                g = routing["gate"][t, 0] if mode == "first_gate_for_all" else routing["gate"][t, c]
+                out[i] += float(g) * ye
+        return out
+    return rows_fn
+
+
+def _route_and_dispatch_no_capacity(wl, inputs):
+    r = _orig["route_and_dispatch"](wl, inputs)
+    idx = r["expert_idx"]
+    slot, count, st = O.dispatch(idx, wl.E, wl.T * wl.k)
+    return dict(r, slot=slot, expert_count=count, slot_token=st[:, :r["capacity"]])
+
+
 def _splitmix_bad_shift(seed, n):
     out, state, M = [], seed, (1 << 64) - 1
     for _ in range(n):
@@ -263,6 +291,7 @@ ALL_PINS = [
     P.check_topk_rank, P.check_gate_raw, lambda rng: P.check_splitmix_reference(), P.check_rre,
     P.check_dispatch_invariants, P.check_dispatch_no_drop, P.check_choice_priority,
     lambda rng: P.check_gelu_values(), P.check_dense_equals_sparse, P.check_single_expert_is_mlp,
+    P.check_forward_rows, P.check_route_and_dispatch,
     P.check_glu_coordinate_gate, P.check_glu_linear_in_v,
     P.check_k_equals_E_is_softmax_mixture, P.check_expert_permutation, P.check_aux_loss,
     P.check_backward_autograd, P.check_backward_finite_differences,
@@ -289,6 +318,9 @@ MUTATIONS = {
     "glu_units_mispaired": ("expert_hidden", _glu_hidden_variant("mispaired")),
     "backward_glu_gate_half_uses_act_grad": ("backward", _backward_glu_variant("gate_half_uses_act_grad")),
     "backward_glu_act_half_without_gate": ("backward", _backward_glu_variant("act_half_without_gate")),
+    "forward_rows_first_choice_only": ("forward_rows", _forward_rows_variant("first_choice_only")),
+    "forward_rows_first_gate_for_all": ("forward_rows", _forward_rows_variant("first_gate_for_all")),
+    "route_and_dispatch_without_capacity": ("route_and_dispatch", _route_and_dispatch_no_capacity),
     "splitmix_wrong_shift": ("splitmix64", _splitmix_bad_shift),
     "rre_off_by_one_token": ("route_rre", _rre_shifted),
     "gelu_grad_without_density_term": ("act_grad", _gelu_grad_no_density),

@@ -72,6 +72,14 @@ def test_dense_equals_sparse(rng):
     P.check_dense_equals_sparse(rng)
 
 
+def test_forward_rows(rng):
+    P.check_forward_rows(rng)
+
+
+def test_route_and_dispatch(rng):
+    P.check_route_and_dispatch(rng)
+
+
 def test_glu_coordinate_gate(rng):
     P.check_glu_coordinate_gate(rng)
 
