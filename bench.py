@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=25.0,
                     help="bound on the oracle's CPU time for the baseline sample")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time only the forward and its step-wise kernels (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain copy of known size (counter calibration runs)")
     return ap.parse_args()
@@ -217,10 +219,28 @@ def main():
         "gemm_up": timed(lambda: moe.expert_up(cfg, x_e, cnt_t, w1, hidden, stream), R),
         "gemm_down": timed(lambda: moe.expert_down(cfg, hidden, cnt_t, w2, y_e, stream), R),
     }
-    if wl.route == "topk":  # router + load-balancing loss (Eq. 4-6)
-        aux_t = torch.empty(1 + 2 * wl.E, dtype=torch.float32, device=dev)
-        kern_us["router_aux"] = timed(
-            lambda: moe.router_aux(cfg, x, w_r, bias, idx2, gate2, 1e-2, aux_t, ws, stream), R)
+    if not args.forward_only:
+        if wl.route == "topk":  # router + load-balancing loss (Eq. 4-6)
+            aux_t = torch.empty(1 + 2 * wl.E, dtype=torch.float32, device=dev)
+            kern_us["router_aux"] = timed(
+                lambda: moe.router_aux(cfg, x, w_r, bias, idx2, gate2, 1e-2, aux_t, ws, stream), R)
+        training_extras(args, wl, cfg, x, w_r, bias, gid, w1, w2, y, y2, ws, x_e, cnt_t, hidden, y_e,
+                        idx2, gate2, elem, dev, stream, timed, kern_us)
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        kern_us["copy_256MiB"] = timed(lambda: dst.copy_(src), R)
+    report(args, wl, C, active, served, drops, kern_us, isolated_us, keep_host, inputs, host_w1, host_w2,
+           tokens_per_s, ms_per_step, ev_ms, t_gen)
+
+
+def training_extras(args, wl, cfg, x, w_r, bias, gid, w1, w2, y, y2, ws, x_e, cnt_t, hidden, y_e,
+                    idx2, gate2, elem, dev, stream, timed, kern_us):
+    """Calls outside the timed step: backward, SparseClip, single-launch FFN, GeGLU experts."""
+    import torch
+
+    import sparse_mixture_experts_13_amd as moe
+    R = args.kernel_reps
     # backward of the layer (training): gradients for an upstream dy, after the forward above
     # (ws holds the forward results of the last timed step)
     dy_t = torch.randn((wl.T, wl.d_model), device=dev).to(y.dtype)
@@ -259,11 +279,12 @@ def main():
                                                              dbias_t, dw1g, dw2g, ws_g, bws_g, stream),
                                         max(2, R // 2))
         del w1g, dw1g, dw2g, bws_g, ws_g
-    if args.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        kern_us["copy_256MiB"] = timed(lambda: dst.copy_(src), R)
 
+
+def report(args, wl, C, active, served, drops, kern_us, isolated_us, keep_host, inputs, host_w1, host_w2,
+           tokens_per_s, ms_per_step, ev_ms, t_gen):
+    """Roofline of the dominant kernel, per-kernel rates, CPU baseline; prints the JSON line."""
+    es = 2 if wl.dtype == "bf16" else 4
     # algorithmic bytes / flops per launch (served rows only; weights of experts with tokens)
     d, f = wl.d_model, wl.d_ff
     wbytes = active * d * f * es

@@ -831,7 +831,6 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
 // element sees the same MFMA operands in the same k order as in the two-launch
 // path, so the results are identical to it.
 // ---------------------------------------------------------------------------
-constexpr int kFusedFC = 128;    // d_ff chunk per hidden tile
 constexpr int kFusedRows = 192;  // rows per stage: 128 of w1 + 64 activations, or 192 of w2
 
 template <int S>
@@ -1273,16 +1272,6 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
   if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 128) return run_ring<4, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   return run_ring<5, 2, 1, 4, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-}
-
-// Column groups per expert for the fused FFN, or 0 where it does not apply:
-// bf16, capacity <= 64, d_ff a multiple of 128, and d_model a multiple of 384
-// split into column groups of 384 (NH = 2: 64 accumulator registers per lane;
-// wider groups spill).
-int fused_ffn_split(const Plan& p) {
-  if (p.glu || p.dtype != 1 || p.C > 64 || p.C < 1 || p.f % kFusedFC != 0 || p.d % 384 != 0) return 0;
-  if (p.d * p.f >= (int64_t(1) << 31)) return 0;  // 32-bit offsets inside one expert
-  return static_cast<int>(p.d / 384);
 }
 
 hipError_t launch_expert_ffn_fused(const Plan& p, int nspl, const void* x_e,

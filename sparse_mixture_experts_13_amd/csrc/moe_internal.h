@@ -56,8 +56,16 @@ hipError_t launch_expert_ffn(const Plan& p, const void* x_e, const int32_t* expe
                              const void* w1, const void* w2, void* y_e, void* ws, hipStream_t s);
 hipError_t launch_expert_up(const Plan& p, const void* x_e, const int32_t* expert_count,
                             const void* w1, void* hidden, hipStream_t s);
-// Fused FFN (bf16, capacity <= 64): column groups per expert, 0 if not applicable.
-int fused_ffn_split(const Plan& p);
+// Fused FFN (bf16, capacity <= 64): column groups per expert, 0 if not applicable:
+// bf16, capacity <= 64, d_ff a multiple of the 128-column hidden chunk, and d_model a
+// multiple of 384 split into column groups of 384 (two 192-column accumulator tiles
+// per wave: 64 registers per lane; wider groups spill).
+constexpr int kFusedFC = 128;  // d_ff chunk per hidden tile
+inline int fused_ffn_split(const Plan& p) {
+  if (p.glu || p.dtype != 1 || p.C > 64 || p.C < 1 || p.f % kFusedFC != 0 || p.d % 384 != 0) return 0;
+  if (p.d * p.f >= (int64_t(1) << 31)) return 0;  // 32-bit offsets inside one expert
+  return static_cast<int>(p.d / 384);
+}
 // y_e = act(x_e W1) W2 in one launch, the hidden activations kept on chip.
 hipError_t launch_expert_ffn_fused(const Plan& p, int nspl, const void* x_e,
                                    const int32_t* expert_count, const void* w1, const void* w2,
