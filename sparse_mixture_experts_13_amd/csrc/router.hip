@@ -15,7 +15,8 @@
 // when the weight is bf16-exact (mid = lo = 0, detected on the device) only the
 // hi plane is used.  Weight and token rows stream through an LDS stage ring fed
 // by direct global->LDS loads; the logits tile then goes to LDS, and sixteen
-// lanes rank each token with 64-bit keys (logit, then lower index).  The block's
+// lanes (one DPP row) rank each token by (logit, then lower index) with
+// cross-lane DPP moves.  The block's
 // expert histogram is built in LDS for the dispatch scan.  float32 tokens use a
 // float32 FMA kernel with the same ranking, 64 tokens per block.
 //
@@ -31,22 +32,43 @@
 
 namespace moe {
 
-// ---- total order on (logit desc, expert asc) as one unsigned 64-bit key ----
-__device__ __forceinline__ uint32_t ordered_bits(float h) {
-  uint32_t u = __float_as_uint(h);
-  if (h == 0.0f) u = 0u;  // -0 ranks equal to +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// ---- ranking inside a 16-lane DPP row: (logit desc, expert asc) ----
+// Float comparison ranks -0 equal to +0, so equal logits (either sign of zero)
+// fall to the lower expert index.
+__device__ __forceinline__ void best_merge(float& v, int& e, float v2, int e2) {
+  const bool take = (v2 > v) | ((v2 == v) & (e2 < e));  // bitwise: no branches
+  v = take ? v2 : v;
+  e = take ? e2 : e;
 }
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  uint32_t o = static_cast<uint32_t>(key >> 32);
-  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-  return __uint_as_float(u);
+
+// One exchange step across the row: rotate by 8 or 4 lanes, then swap within
+// pairs of lanes of a quad (row_ror:8 and row_ror:4, quad_perm [2,3,0,1] and
+// [1,0,3,2]); after the four steps every lane of the row holds the row's
+// result.  DPP moves go through the VALU, not the LDS crossbar.
+template <int CTRL>
+__device__ __forceinline__ int dpp_row(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ uint64_t make_key(float h, int e) {
-  return (static_cast<uint64_t>(ordered_bits(h)) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - e);
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& v, int& e) {
+  const float v2 = __int_as_float(dpp_row<CTRL>(__float_as_int(v)));
+  const int e2 = dpp_row<CTRL>(e);
+  best_merge(v, e, v2, e2);
 }
-__device__ __forceinline__ int key_expert(uint64_t key) {
-  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+__device__ __forceinline__ void row16_best(float& v, int& e) {
+  best_step<0x128>(v, e);
+  best_step<0x124>(v, e);
+  best_step<0x4E>(v, e);
+  best_step<0xB1>(v, e);
+}
+// Sum over the row.  Lanes i and i+8 (then i and i+4, ...) add the same two
+// values in either order, so every lane ends with the same bits.
+__device__ __forceinline__ float row16_sum(float s) {
+  s += __int_as_float(dpp_row<0x128>(__float_as_int(s)));
+  s += __int_as_float(dpp_row<0x124>(__float_as_int(s)));
+  s += __int_as_float(dpp_row<0x4E>(__float_as_int(s)));
+  s += __int_as_float(dpp_row<0xB1>(__float_as_int(s)));
+  return s;
 }
 
 __device__ __forceinline__ void write_hist(const int* hl, int ldh, int E, int k, int NB, int b,
@@ -125,9 +147,9 @@ __host__ __device__ inline int64_t router_lg_bytes(int TB, int Epad) {
 
 // Rank the tokens of a block from the logits tile lg [TB][ld] in LDS (both
 // routers).  Sixteen lanes share a token (a wave ranks four tokens at a time);
-// lane `sub` holds experts sub, sub+16, ...  Keys order by (logit desc, expert asc).
+// lane `sub` holds experts sub, sub+16, ...  Choices order by (logit desc, expert asc).
 template <int NV>
-__device__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int ntok, int E, int k,
+__device__ __forceinline__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int ntok, int E, int k,
                                 const float* __restrict__ bias, int32_t* __restrict__ expert_idx,
                                 float* __restrict__ gate, int* hl, int ldh, int wave, int lane,
                                 float* __restrict__ psum, float* red, float* __restrict__ hout,
@@ -141,53 +163,61 @@ __device__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int n
     // round wait for the previous round's stores (loads and stores share vmcnt)
     bv[i] = bias && sub + 16 * i < E ? bias[sub + 16 * i] : 0.f;
   }
+  constexpr float kLog2e = 1.4426950408889634f;
   for (int base = 0; base < TB; base += 16) {
     const int t = base + wave * 4 + grp;
     const bool valid = t < ntok;
+    // every read is inside the tile (t < TB rows, e < Epad <= ld columns); the
+    // values past the token count or past E are then replaced by -inf, so the
+    // loop has no branches
+    const float* row = lg + (valid ? t : 0) * ld;
     float hv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = sub + 16 * i;
-      hv[i] = -INFINITY;
-      if (valid && e < E) {
-        float h = lg[t * ld + e];
-        if (bias) h = h + bv[i];  // one float32 rounding after the full dot product
-        hv[i] = h;
-        if (hout) hout[static_cast<int64_t>(tok0 + t) * ldo + e] = h;
-      }
+      const float h = row[e];
+      const float hb = bias ? h + bv[i] : h;  // one float32 rounding after the full dot product
+      hv[i] = (valid & (e < E)) ? hb : -INFINITY;
     }
+    if (hout && valid) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (sub + 16 * i < E) hout[static_cast<int64_t>(tok0 + t) * ldo + sub + 16 * i] = hv[i];
+    }
+    // choice c: each lane's best remaining expert (its experts ascend with i, so a
+    // strict comparison keeps the lowest index of equal logits), then the row's
     uint32_t removed = 0;
-    uint64_t best0 = 0, mine = 0;
+    float hmax = -INFINITY, vmine = -INFINITY;
+    int emine = 0;
     for (int c = 0; c < k; ++c) {
-      uint64_t m = 0;
+      float v = -INFINITY;
+      int ev = 0x7FFFFFFF;
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        const int e = sub + 16 * i;
-        const uint64_t key = (e < E && !((removed >> i) & 1u)) ? make_key(hv[i], e) : 0ull;
-        m = key > m ? key : m;
+        const bool take = (((removed >> i) & 1u) == 0u) & (hv[i] > v);
+        v = take ? hv[i] : v;
+        ev = take ? sub + 16 * i : ev;
       }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        const uint64_t w = __shfl_xor(m, o, kWave);
-        m = w > m ? w : m;
+      row16_best(v, ev);
+      if (ev < E && (ev & 15) == sub) removed |= 1u << (ev >> 4);
+      if (c == 0) hmax = v;
+      if (sub == c) {
+        vmine = v;
+        emine = ev;
       }
-      const int ew = key_expert(m);
-      if ((ew & 15) == sub) removed |= 1u << (ew >> 4);
-      if (c == 0) best0 = m;
-      if (sub == c) mine = m;
     }
-    const float hmax = key_logit(best0);
+    // softmax denominator with the native exp2 (one rounding of (h - hmax) log2 e
+    // and the instruction's own error: the sum is dominated by terms near the
+    // maximum, so its relative error stays near 1e-6); exp(-inf) = 0 past E
     float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) sum += expf(hv[i] - hmax);  // exp(-inf) = 0
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+    for (int i = 0; i < NV; ++i) sum += __builtin_amdgcn_exp2f((hv[i] - hmax) * kLog2e);
+    sum = row16_sum(sum);
     if (valid && sub < k) {
-      const int e = key_expert(mine);
       const int64_t o = static_cast<int64_t>(tok0 + t) * k + sub;
-      expert_idx[o] = e;
-      gate[o] = expf(key_logit(mine) - hmax) / sum;
-      atomicAdd(&hl[sub * ldh + e], 1);
+      expert_idx[o] = emine;
+      gate[o] = expf(vmine - hmax) / sum;
+      atomicAdd(&hl[sub * ldh + emine], 1);
     }
     if (psum && valid) {
 #pragma unroll
