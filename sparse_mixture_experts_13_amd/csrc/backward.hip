@@ -583,20 +583,26 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
     p[i] = 0.f;
 }
 
-// dbias[e] = sum over tokens of dh[t][e] in token order, 16 tokens in flight
-__global__ __launch_bounds__(64) void bwd_bias_kernel(const float* __restrict__ dh, int ldh, int ntok,
-                                                      int E, float* __restrict__ dbias) {
+// dbias partials: block (x, y) adds dh[t][e] over token range y of S (fixed by T and
+// S only) for experts x*64 .. x*64+63, in token order, sixteen rows in flight;
+// part[y][e].  sum_slices_kernel then adds the S ranges in order, so the result is
+// the same on every call.
+__global__ __launch_bounds__(64) void bwd_bias_partial_kernel(const float* __restrict__ dh, int ldh, int ntok,
+                                                              int E, float* __restrict__ part) {
   const int e = blockIdx.x * 64 + threadIdx.x;
+  const int y = blockIdx.y, S = gridDim.y;
   if (e >= E) return;
+  const int t0 = static_cast<int>(static_cast<int64_t>(y) * ntok / S);
+  const int t1 = static_cast<int>(static_cast<int64_t>(y + 1) * ntok / S);
   float acc = 0.f;
-  for (int t = 0; t < ntok; t += 16) {
+  for (int t = t0; t < t1; t += 16) {
     float v[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = t + j < ntok ? dh[static_cast<int64_t>(t + j) * ldh + e] : 0.f;
+    for (int j = 0; j < 16; ++j) v[j] = t + j < t1 ? dh[static_cast<int64_t>(t + j) * ldh + e] : 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc += v[j];
   }
-  dbias[e] = acc;
+  part[static_cast<int64_t>(y) * E + e] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -796,8 +802,14 @@ static hipError_t backward_typed(const Plan& p, const BwdArgs& a, hipStream_t s)
                        dim3(256), 0, s, a.dwr_part, n, KS, a.dw_r);
     MOE_TRY(hipGetLastError());
     if (a.dbias) {
-      hipLaunchKernelGGL(bwd_bias_kernel, dim3((p.E + 63) / 64), dim3(64), 0, s, a.dh, p.Epad, T_, p.E,
-                         a.dbias);
+      // dbias[e] = sum_t dh[t][e]: kBwdSplit token ranges (fewer for short inputs) into
+      // the dw_r partial buffer, free again once dw_r is summed (stream order), then
+      // the ranges added in order
+      const int SB = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kBwdSplit, T_)));
+      hipLaunchKernelGGL(bwd_bias_partial_kernel, dim3((p.E + 63) / 64, SB), dim3(64), 0, s, a.dh, p.Epad,
+                         T_, p.E, a.dwr_part);
+      hipLaunchKernelGGL(sum_slices_kernel, dim3((p.E + 255) / 256), dim3(256), 0, s, a.dwr_part,
+                         int64_t(p.E), SB, a.dbias);
       MOE_TRY(hipGetLastError());
     }
   }

@@ -81,8 +81,10 @@ class Dev:
         self.w2 = to_dev(inputs["w2"]) if inputs.get("w2") is not None else None
         self.ws = moe.alloc_workspace(self.cfg)
 
-    def upload_weights_per_expert(self):
-        """Generate and upload every expert's weights without a host-side stack."""
+    def upload_weights_per_expert(self, on_expert=None):
+        """Generate and upload every expert's weights without a host-side stack;
+        ``on_expert(e, w1_e, w2_e)`` (optional) also sees each expert's host arrays
+        (called from the generator's pool threads)."""
         wl = self.wl
         dt = elem_dtype(wl)
         self.w1 = torch.empty((wl.E, W.w1_rows(wl), wl.d_model), dtype=dt, device=DEV)
@@ -91,6 +93,8 @@ class Dev:
         def put(e, a, b):
             self.w1[e].copy_(to_dev(a))
             self.w2[e].copy_(to_dev(b))
+            if on_expert is not None:
+                on_expert(e, a, b)
 
         W.for_each_expert(wl, put, threads=8)
         torch.cuda.synchronize()

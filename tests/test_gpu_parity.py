@@ -288,6 +288,16 @@ def test_capacity_kernel_ranges(cf, kernel):
     ref, _ = _run_case(wl, inputs, f"C={oracle.capacity(wl.T, wl.E, wl.k, cf)} {kernel}")
 
 
+@pytest.mark.parametrize("E,T,k,block", [(200, 1000, 2, "32 tokens x 256 experts"),
+                                         (200, 20000, 2, "64 tokens x 256 experts"),
+                                         (100, 32768, 1, "128 tokens x 128 experts")])
+def test_router_block_shapes(E, T, k, block):
+    """The bf16 router's block shapes chosen from (E, T) that the other workloads do not
+    reach: routing, slots, counts and slot maps bit-exact, layer output in tolerance."""
+    wl = BASE.replace(T=T, E=E, k=k, d_model=64, d_ff=64, capacity_factor=1.25)
+    _run_case(wl, W.make_inputs(wl), f"router block {block} (E={E}, T={T}, k={k})")
+
+
 def test_one_expert_takes_all():
     wl = BASE.replace(T=500, E=16, k=2, capacity_factor=1.25)
     inputs = W.make_inputs(wl)
