@@ -220,6 +220,26 @@ int moe_forward(const moe_config* cfg, const void* x, const float* w_r, const fl
                 const int32_t* group_id, const void* w1, const void* w2, void* y, void* ws,
                 void* stream);
 
+/* moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as moe_forward minus `ws`:
+ * the intermediates go to a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * (80 MiB, enough for a Switch-Base-sized layer: E = 128, capacity 64,
+ * d_model 768, d_ff 3072 needs 73.2 MiB) that each GPU the library runs on holds
+ * from the first call on it until the process ends.  Nothing in the call
+ * allocates.  Nothing in the scratch needs to start at zero: every kernel writes
+ * what it later reads.  Every call on one GPU shares that GPU's array and leaves
+ * its intermediates there, laid out as moe_workspace_offset describes, until the
+ * next call; calls that overlap on one GPU (other streams, other threads) race
+ * on it and must be serialised by the caller.
+ * MOE_ERR_UNSUPPORTED (nothing launched) when moe_workspace_bytes(cfg) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES; MOE_ERR_HIP if the array's device address cannot be
+ * obtained on the current device. */
+#define MOE_NOALLOC_SCRATCH_BYTES (80LL << 20)
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
+                        const int32_t* group_id, const void* w1, const void* w2, void* y,
+                        void* stream);
+
 /* Bytes of the second device workspace moe_backward needs (`bws`: its scratch;
  * the forward workspace `ws` keeps the forward's results).  Negative status on an
  * invalid configuration. */

@@ -19,7 +19,8 @@ from ._lib import ACT, DTYPE, EXPORTS, REGION, ROUTE, MoeConfig, load  # noqa: F
 
 __all__ = ["MoeConfig", "MoeError", "make_config", "config_for", "capacity", "workspace_bytes",
            "workspace_offset", "alloc_workspace", "workspace_view", "router", "router_aux", "dispatch",
-           "expert_ffn", "expert_ffn_fused", "expert_up", "expert_down", "combine", "forward", "backward_workspace_bytes", "alloc_backward_workspace",
+           "expert_ffn", "expert_ffn_fused", "expert_up", "expert_down", "combine", "forward", "forward_noalloc",
+           "NOALLOC_SCRATCH_BYTES", "backward_workspace_bytes", "alloc_backward_workspace",
            "backward", "sparse_clip", "version", "load"]
 
 
@@ -180,6 +181,15 @@ def sparse_clip(cfg, dw_r, dbias, dw1, dw2, max_norm, norm_coef, bws, stream=Non
 def forward(cfg, x, w_r, bias, group_id, w1, w2, y, ws, stream=None) -> None:
     _status(load().moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_r), _ptr(bias), _ptr(group_id),
                                _ptr(w1), _ptr(w2), _ptr(y), _ptr(ws), _stream(stream)))
+
+
+def forward_noalloc(cfg, x, w_r, bias, group_id, w1, w2, y, stream=None) -> None:
+    """moe_forward on the library's static per-GPU scratch (no workspace argument)."""
+    _status(load().moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(w_r), _ptr(bias), _ptr(group_id),
+                                       _ptr(w1), _ptr(w2), _ptr(y), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 80 << 20
 
 
 def version() -> str:

@@ -15,7 +15,7 @@ REGION = {"expert_idx": 0, "gate": 1, "slot": 2, "expert_count": 3, "slot_token"
           "x_e": 5, "hidden": 6, "y_e": 7}
 
 EXPORTS = ["moe_capacity", "moe_workspace_bytes", "moe_workspace_offset", "moe_router", "moe_router_aux",
-           "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_fused", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_backward_workspace_bytes", "moe_backward", "moe_sparse_clip", "moe_last_error",
+           "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_fused", "moe_expert_up", "moe_expert_down", "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_backward_workspace_bytes", "moe_backward", "moe_sparse_clip", "moe_last_error",
            "moe_version"]
 
 
@@ -74,6 +74,8 @@ def load() -> ctypes.CDLL:
     lib.moe_combine.restype = ctypes.c_int
     lib.moe_forward.argtypes = [cfgp, P, P, P, P, P, P, P, P, P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [cfgp, P, P, P, P, P, P, P, P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_backward_workspace_bytes.argtypes = [cfgp]
     lib.moe_backward_workspace_bytes.restype = i64
     lib.moe_backward.argtypes = [cfgp] + [P] * 13

@@ -373,12 +373,12 @@ int moe_combine(const moe_config* cfg, const void* y_e, const int32_t* expert_id
   return MOE_OK;
 }
 
-int moe_forward(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
-                const int32_t* group_id, const void* w1, const void* w2, void* y, void* ws,
-                void* stream) {
-  MOE_CHECK(validate(cfg));
-  moe::Plan p;
-  make_plan(cfg, p);
+}  // extern "C"
+
+namespace {
+
+int check_forward_args(const moe::Plan& p, const void* x, const float* w_r, const int32_t* group_id,
+                       const void* w1, const void* w2, const void* y) {
   const int64_t wbytes = int64_t(p.E) * p.d * p.f * p.elem;
   MOE_CHECK(need(x, p.T * p.d * p.elem, "x"));
   if (p.route == MOE_ROUTE_TOPK) MOE_CHECK(need(w_r, 1, "w_r"));
@@ -386,8 +386,13 @@ int moe_forward(const moe_config* cfg, const void* x, const float* w_r, const fl
   MOE_CHECK(need(w1, wbytes / p.f * p.w1_rows(), "w1"));
   MOE_CHECK(need(w2, wbytes, "w2"));
   MOE_CHECK(need(y, p.T * p.d * p.elem, "y"));
-  MOE_CHECK(need(ws, p.total, "ws"));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return MOE_OK;
+}
+
+// The launch sequence of the whole layer on the workspace `ws` (validated).
+int run_forward(const moe::Plan& p, const void* x, const float* w_r, const float* bias,
+                const int32_t* group_id, const void* w1, const void* w2, void* y, void* ws,
+                hipStream_t s) {
   char* base = static_cast<char*>(ws);
   auto* expert_idx = reinterpret_cast<int32_t*>(base + p.off_region[MOE_WS_EXPERT_IDX]);
   auto* gate = reinterpret_cast<float*>(base + p.off_region[MOE_WS_GATE]);
@@ -404,6 +409,41 @@ int moe_forward(const moe_config* cfg, const void* x, const float* w_r, const fl
   MOE_HIP(moe::launch_expert_ffn(p, x_e, count, w1, w2, y_e, ws, s), "expert ffn");
   MOE_HIP(moe::launch_combine(p, y_e, expert_idx, slot, gate, y, s), "combine");
   return MOE_OK;
+}
+
+static_assert(moe::kNoAllocScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "scratch size");
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
+                const int32_t* group_id, const void* w1, const void* w2, void* y, void* ws,
+                void* stream) {
+  MOE_CHECK(validate(cfg));
+  moe::Plan p;
+  make_plan(cfg, p);
+  MOE_CHECK(check_forward_args(p, x, w_r, group_id, w1, w2, y));
+  MOE_CHECK(need(ws, p.total, "ws"));
+  return run_forward(p, x, w_r, bias, group_id, w1, w2, y, ws, static_cast<hipStream_t>(stream));
+}
+
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
+                        const int32_t* group_id, const void* w1, const void* w2, void* y,
+                        void* stream) {
+  MOE_CHECK(validate(cfg));
+  moe::Plan p;
+  make_plan(cfg, p);
+  MOE_CHECK(check_forward_args(p, x, w_r, group_id, w1, w2, y));
+  if (p.total > moe::kNoAllocScratchBytes) {
+    g_last_error = "moe_forward_noalloc: this configuration needs " + std::to_string(p.total) +
+                   " bytes of scratch; the static scratch holds " + std::to_string(moe::kNoAllocScratchBytes) +
+                   " (use moe_forward with a workspace)";
+    return MOE_ERR_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  MOE_HIP(moe::noalloc_scratch(&ws), "static scratch address");
+  return run_forward(p, x, w_r, bias, group_id, w1, w2, y, ws, static_cast<hipStream_t>(stream));
 }
 
 int64_t moe_backward_workspace_bytes(const moe_config* cfg) {

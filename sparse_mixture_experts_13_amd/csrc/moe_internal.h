@@ -131,6 +131,12 @@ hipError_t launch_sparse_clip(const Plan& p, float* dw_r, float* dbias, void* dw
 hipError_t launch_combine(const Plan& p, const void* y_e, const int32_t* expert_idx,
                           const int32_t* slot, const float* gate, void* y, hipStream_t s);
 
+// scratch.hip: the static per-device scratch of moe_forward_noalloc.
+constexpr int64_t kNoAllocScratchBytes = 80LL << 20;
+// Device address of the scratch array on the current device (looked up once per
+// device, then cached); hipErrorInvalidDevice for a device ordinal past 63.
+hipError_t noalloc_scratch(void** out);
+
 inline char* ws_at(void* ws, int64_t off) { return static_cast<char*>(ws) + off; }
 
 }  // namespace moe

@@ -35,6 +35,10 @@ hipError_t launch_backward(const Plan&, const BwdArgs&, hipStream_t) { return no
 hipError_t launch_sparse_clip(const Plan&, float*, float*, void*, void*, double, float*, void*, hipStream_t) {
   return no_device();
 }
+hipError_t noalloc_scratch(void** out) {
+  *out = nullptr;
+  return no_device();
+}
 hipError_t launch_combine(const Plan&, const void*, const int32_t*, const int32_t*, const float*, void*,
                           hipStream_t) { return no_device(); }
 

@@ -293,3 +293,29 @@ def test_glu_configs_accepted_and_sized():
         grow = lib.moe_backward_workspace_bytes(ctypes.byref(b)) - \
             lib.moe_backward_workspace_bytes(ctypes.byref(a))
         assert 2 * half + half - zplain <= grow <= 2 * half + half - zplain + 2 * 256
+
+
+def test_forward_noalloc_host_checks():
+    """moe_forward_noalloc: the same argument checks as moe_forward (no ws argument),
+    and a configuration whose workspace exceeds the static scratch is rejected before
+    any HIP call."""
+    lib = moe.load()
+    ok = ctypes.c_void_p(0x100000)
+    cfg = _cfg()
+    args = [ok, ok, None, None, ok, ok, ok, None]
+    for i, name in [(0, "x"), (1, "w_r"), (6, "y"), (4, "w1"), (5, "w2")]:
+        a = list(args)
+        a[i] = None
+        assert lib.moe_forward_noalloc(ctypes.byref(cfg), *a) == _lib.MOE_ERR_ARG
+        assert lib.moe_last_error().decode().startswith(name + " ")
+    assert lib.moe_forward_noalloc(None, *args) == _lib.MOE_ERR_ARG
+    import moe_workloads as W
+    for name, fits in [("switch_base_bf16", True), ("tiny_switch_f32", True), ("xmoe_top2_bf16", False),
+                       ("large_zipf_top2_bf16", False)]:
+        c = moe.config_for(W.WORKLOADS[name])
+        assert (lib.moe_workspace_bytes(ctypes.byref(c)) <= moe.NOALLOC_SCRATCH_BYTES) == fits, name
+        if not fits:
+            assert lib.moe_forward_noalloc(ctypes.byref(c), *args) == _lib.MOE_ERR_UNSUPPORTED
+            msg = lib.moe_last_error().decode()
+            assert "scratch" in msg and str(moe.NOALLOC_SCRATCH_BYTES) in msg, msg
+    assert moe.NOALLOC_SCRATCH_BYTES == 80 << 20
