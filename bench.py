@@ -31,7 +31,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 FP32_PEAK_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = [os.path.join(ROOT, "sparse_mixture_experts_13_amd", "csrc", name)
-              for name in ("expert_ffn.hip", "moe_common.h")]
+              for name in ("expert_ffn.hip", "router.hip", "dispatch.hip", "combine.hip", "moe_common.h")]
 
 
 def parse():
@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=25.0,
                     help="bound on the oracle's CPU time for the baseline sample")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other layers of the workload table (the 'configs' field)")
+    ap.add_argument("--config-steps", type=int, default=10, help="timed steps per other layer")
     ap.add_argument("--forward-only", action="store_true",
                     help="time only the forward and its step-wise kernels (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -165,16 +168,8 @@ def main():
     hidden = moe.workspace_view(ws, cfg, "hidden")
     y_e = moe.workspace_view(ws, cfg, "y_e")
     cnt_t = moe.workspace_view(ws, cfg, "expert_count")
-    idx_t = moe.workspace_view(ws, cfg, "expert_idx")
-    gate_t = moe.workspace_view(ws, cfg, "gate")
-    slot_t = moe.workspace_view(ws, cfg, "slot")
-    st_t = moe.workspace_view(ws, cfg, "slot_token")
-    idx2 = torch.empty_like(idx_t)
-    gate2 = torch.empty_like(gate_t)
-    slot2 = torch.empty_like(slot_t)
-    cnt2 = torch.empty_like(cnt_t)
-    st2 = torch.empty_like(st_t)
-    xe2 = torch.empty_like(x_e)
+    idx2 = torch.empty_like(moe.workspace_view(ws, cfg, "expert_idx"))
+    gate2 = torch.empty_like(moe.workspace_view(ws, cfg, "gate"))
     y2 = torch.empty_like(y)
 
     def timed(fn, reps):
@@ -193,27 +188,7 @@ def main():
     # moe_forward launches, plus the dispatch call's own histogram pass), an event on the
     # launch stream between consecutive calls, so each duration is the kernel in the
     # context of the step (the previous kernel's output in flight, a cold weight stream).
-    hidden2, ye2 = torch.empty_like(hidden), torch.empty_like(y_e)
-    seq_names = ["router", "dispatch", "gemm_up", "gemm_down", "combine"]
-    seq_calls = [lambda: moe.router(cfg, x, w_r, bias, gid, idx2, gate2, ws, stream),
-                 lambda: moe.dispatch(cfg, x, idx2, slot2, cnt2, st2, xe2, ws, stream),
-                 lambda: moe.expert_up(cfg, xe2, cnt2, w1, hidden2, stream),
-                 lambda: moe.expert_down(cfg, hidden2, cnt2, w2, ye2, stream),
-                 lambda: moe.combine(cfg, ye2, idx2, slot2, gate2, y2, stream)]
-
-    def in_step(n):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq_calls) + 1)] for _ in range(n)]
-        for i in range(n):
-            evs[i][0].record(stream)
-            for j, call in enumerate(seq_calls):
-                call()
-                evs[i][j + 1].record(stream)
-        torch.cuda.synchronize()
-        return {nm: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(n)) * 1e3 / n
-                for j, nm in enumerate(seq_names)}
-
-    in_step(2)
-    kern_us = in_step(args.steps)
+    kern_us = step_kernels(moe, cfg, wl, x, w_r, bias, gid, w1, w2, ws, stream, args.steps)
     # the same launches repeated alone (back to back, warm caches): for reference
     isolated_us = {
         "gemm_up": timed(lambda: moe.expert_up(cfg, x_e, cnt_t, w1, hidden, stream), R),
@@ -230,8 +205,13 @@ def main():
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         kern_us["copy_256MiB"] = timed(lambda: dst.copy_(src), R)
+    configs = None
+    if not args.no_configs:
+        del w1, w2, ws
+        torch.cuda.empty_cache()
+        configs = config_sweep(args, wl.name)
     report(args, wl, C, active, served, drops, kern_us, isolated_us, keep_host, inputs, host_w1, host_w2,
-           tokens_per_s, ms_per_step, ev_ms, t_gen)
+           tokens_per_s, ms_per_step, ev_ms, t_gen, configs)
 
 
 def training_extras(args, wl, cfg, x, w_r, bias, gid, w1, w2, y, y2, ws, x_e, cnt_t, hidden, y_e,
@@ -281,15 +261,13 @@ def training_extras(args, wl, cfg, x, w_r, bias, gid, w1, w2, y, y2, ws, x_e, cn
         del w1g, dw1g, dw2g, bws_g, ws_g
 
 
-def report(args, wl, C, active, served, drops, kern_us, isolated_us, keep_host, inputs, host_w1, host_w2,
-           tokens_per_s, ms_per_step, ev_ms, t_gen):
-    """Roofline of the dominant kernel, per-kernel rates, CPU baseline; prints the JSON line."""
+def algo_work(wl, served, active):
+    """Algorithmic bytes and flops per launch (served rows only; weights of experts with tokens)."""
     es = 2 if wl.dtype == "bf16" else 4
-    # algorithmic bytes / flops per launch (served rows only; weights of experts with tokens)
     d, f = wl.d_model, wl.d_ff
     wbytes = active * d * f * es
     g1 = 2 if wl.glu else 1  # GLU: the up-projection reads and multiplies 2 d_ff weight rows
-    algo = {
+    return {
         "gemm_up": dict(bytes=g1 * wbytes + served * d * es + served * f * es, flops=2.0 * g1 * served * d * f),
         "glu_up": dict(bytes=2 * wbytes + served * d * es + served * f * es, flops=4.0 * served * d * f),
         "gemm_down": dict(bytes=wbytes + served * f * es + served * d * es, flops=2.0 * served * d * f),
@@ -302,6 +280,10 @@ def report(args, wl, C, active, served, drops, kern_us, isolated_us, keep_host, 
         "sparse_clip": dict(bytes=3 * wl.E * d * f * (g1 + 1) * es, flops=0.0),
         "sparse_clip_inactive": dict(bytes=wl.E * d * f * (g1 + 1) * es, flops=0.0),
     }
+
+
+def dominant_roofline(wl, algo, kern_us):
+    """Roofline of the slower grouped-GEMM launch: HBM-bound below the bf16 ridge, else MFMA."""
     dom = max(("gemm_up", "gemm_down"), key=lambda n: kern_us[n])
     dom_us = kern_us[dom]
     intensity = algo[dom]["flops"] / algo[dom]["bytes"]
@@ -312,10 +294,13 @@ def report(args, wl, C, active, served, drops, kern_us, isolated_us, keep_host, 
         bound, achieved, peak, unit = "hbm", algo[dom]["bytes"] / dom_us / 1e3, HBM_PEAK_GBS, "GB/s"
     kname = {"gemm_up": "grouped GEMM up-projection + act" + (" + GLU gate" if wl.glu else "") + " (moe_expert_up)",
              "gemm_down": "grouped GEMM down-projection (moe_expert_down)"}[dom]
-    traffic = read_traffic(dom, wl.name)
-    roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kname,
-                "algorithmic_bytes": int(algo[dom]["bytes"]), "us_per_launch": round(dom_us, 2)}
+    return dom, {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                 "frac": round(achieved / peak, 4), "kernel": kname,
+                 "algorithmic_bytes": int(algo[dom]["bytes"]), "us_per_launch": round(dom_us, 2)}
+
+
+def kernel_rates(wl, algo, kern_us):
+    """Per-kernel microseconds, GB/s and fractions of HBM / MFMA peak."""
     peak_flops = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
     kernels = {}
     for n, us in kern_us.items():
@@ -326,6 +311,120 @@ def report(args, wl, C, active, served, drops, kern_us, isolated_us, keep_host, 
             if algo[n]["flops"]:
                 row["mfma_frac"] = round(algo[n]["flops"] / us / 1e6 / peak_flops, 4)
         kernels[n] = row
+    return kernels
+
+
+def gemm_mfma_frac(wl, algo, kern_us):
+    peak_flops = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    return round((algo["gemm_up"]["flops"] + algo["gemm_down"]["flops"]) /
+                 ((kern_us["gemm_up"] + kern_us["gemm_down"]) / 1e6) / (peak_flops * 1e12), 4)
+
+
+def step_kernels(moe, cfg, wl, x, w_r, bias, gid, w1, w2, ws, stream, n):
+    """The forward's kernels inside a step: the step-wise calls in order, an event on the
+    launch stream between consecutive calls; microseconds per call, averaged over n steps."""
+    import torch
+    C = moe.capacity(cfg)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    new = lambda shape, t: torch.empty(shape, dtype=t, device="cuda")  # noqa: E731
+    idx2, gate2 = new((wl.T, wl.k), torch.int32), new((wl.T, wl.k), torch.float32)
+    slot2, cnt2, st2 = new((wl.T, wl.k), torch.int32), new((wl.E,), torch.int32), new((wl.E, C), torch.int32)
+    xe2, ye2 = new((wl.E, C, wl.d_model), dt), new((wl.E, C, wl.d_model), dt)
+    hidden2, y2 = new((wl.E, C, wl.d_ff), dt), new((wl.T, wl.d_model), dt)
+    names = ["router", "dispatch", "gemm_up", "gemm_down", "combine"]
+    calls = [lambda: moe.router(cfg, x, w_r, bias, gid, idx2, gate2, ws, stream),
+             lambda: moe.dispatch(cfg, x, idx2, slot2, cnt2, st2, xe2, ws, stream),
+             lambda: moe.expert_up(cfg, xe2, cnt2, w1, hidden2, stream),
+             lambda: moe.expert_down(cfg, hidden2, cnt2, w2, ye2, stream),
+             lambda: moe.combine(cfg, ye2, idx2, slot2, gate2, y2, stream)]
+
+    def run(m):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(m)]
+        for i in range(m):
+            evs[i][0].record(stream)
+            for j, call in enumerate(calls):
+                call()
+                evs[i][j + 1].record(stream)
+        torch.cuda.synchronize()
+        return {nm: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(m)) * 1e3 / m
+                for j, nm in enumerate(names)}
+
+    run(2)
+    return run(n)
+
+
+def config_sweep(args, skip):
+    """Every other layer of the workload table, timed the same way on device-generated
+    weights (seeded N(0, 1/fan_in), rounded to the layer dtype; routing inputs from the
+    seeded generators): tokens/s, ms/step, the dominant kernel's roofline, per-kernel rates."""
+    import numpy as np
+    import torch
+
+    import moe_workloads as W
+    import sparse_mixture_experts_13_amd as moe
+    out = {}
+    stream = torch.cuda.current_stream()
+    for name, wl in W.WORKLOADS.items():
+        if name == skip:
+            continue
+        t0 = time.time()
+        cfg = moe.config_for(wl)
+        elem = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        inputs = W.make_inputs(wl, with_weights=False)
+
+        def up(a):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+            return torch.from_numpy(a).cuda()
+
+        x, w_r, bias, gid = up(inputs["x"]), up(inputs["w_r"]), up(inputs["bias"]), up(inputs["group_id"])
+        gen = torch.Generator(device="cuda").manual_seed(0)
+        w1 = torch.empty((wl.E, W.w1_rows(wl), wl.d_model), dtype=elem, device="cuda")
+        w2 = torch.empty((wl.E, wl.d_model, wl.d_ff), dtype=elem, device="cuda")
+        for e in range(wl.E):
+            w1[e] = (torch.randn(w1.shape[1:], generator=gen, device="cuda") / wl.d_model ** 0.5).to(elem)
+            w2[e] = (torch.randn(w2.shape[1:], generator=gen, device="cuda") / wl.d_ff ** 0.5).to(elem)
+        y = torch.empty((wl.T, wl.d_model), dtype=elem, device="cuda")
+        ws = moe.alloc_workspace(cfg)
+        for _ in range(3):
+            moe.forward(cfg, x, w_r, bias, gid, w1, w2, y, ws, stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t1 = time.perf_counter()
+        a.record(stream)
+        for _ in range(args.config_steps):
+            moe.forward(cfg, x, w_r, bias, gid, w1, w2, y, ws, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t1) * 1e3 / args.config_steps
+        counts = moe.workspace_view(ws, cfg, "expert_count").cpu().numpy().astype(np.int64)
+        served, active = int(counts.sum()), int((counts > 0).sum())
+        kern_us = step_kernels(moe, cfg, wl, x, w_r, bias, gid, w1, w2, ws, stream, max(3, args.config_steps // 2))
+        algo = algo_work(wl, served, active)
+        _, roof = dominant_roofline(wl, algo, kern_us)
+        out[name] = {"tokens_per_s": round(wl.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+                     "event_ms_per_step": round(a.elapsed_time(b) / args.config_steps, 4),
+                     "dtype": wl.dtype, "T": wl.T, "d_model": wl.d_model, "d_ff": wl.d_ff, "E": wl.E,
+                     "k": wl.k, "capacity": moe.capacity(cfg), "route": wl.route, "act": wl.act,
+                     "roofline": roof, "kernels": kernel_rates(wl, algo, kern_us),
+                     "grouped_gemm_mfma_frac": gemm_mfma_frac(wl, algo, kern_us),
+                     "served_assignments": served, "dropped_assignments": wl.T * wl.k - served,
+                     "setup_s": round(time.time() - t0, 1)}
+        del x, w_r, bias, gid, w1, w2, y, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def report(args, wl, C, active, served, drops, kern_us, isolated_us, keep_host, inputs, host_w1, host_w2,
+           tokens_per_s, ms_per_step, ev_ms, t_gen, configs=None):
+    """Roofline of the dominant kernel, per-kernel rates, CPU baseline; prints the JSON line."""
+    algo = algo_work(wl, served, active)
+    dom, roofline = dominant_roofline(wl, algo, kern_us)
+    roofline["traffic"] = read_traffic(dom, wl.name)
+    kernels = kernel_rates(wl, algo, kern_us)
 
     # ---- CPU baseline: the oracle, on the host cores ----
     cpu = None
@@ -354,13 +453,13 @@ def report(args, wl, C, active, served, drops, kern_us, isolated_us, keep_host, 
         "cpu_baseline": cpu,
         "kernels": kernels,
         "isolated_us": {n: round(v, 2) for n, v in isolated_us.items()},
-        "grouped_gemm_mfma_frac": round((algo["gemm_up"]["flops"] + algo["gemm_down"]["flops"]) /
-                                        ((kern_us["gemm_up"] + kern_us["gemm_down"]) / 1e6) /
-                                        (peak_flops * 1e12), 4),
+        "grouped_gemm_mfma_frac": gemm_mfma_frac(wl, algo, kern_us),
         "served_assignments": served,
         "dropped_assignments": drops,
         "input_setup_s": round(t_gen, 1),
     }
+    if configs:
+        out["configs"] = configs
     print(json.dumps(out), flush=True)
 
 
