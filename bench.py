@@ -404,7 +404,8 @@ def config_sweep(args, skip):
         served, active = int(counts.sum()), int((counts > 0).sum())
         kern_us = step_kernels(moe, cfg, wl, x, w_r, bias, gid, w1, w2, ws, stream, max(3, args.config_steps // 2))
         algo = algo_work(wl, served, active)
-        _, roof = dominant_roofline(wl, algo, kern_us)
+        dom, roof = dominant_roofline(wl, algo, kern_us)
+        roof["traffic"] = read_traffic(dom, name)
         out[name] = {"tokens_per_s": round(wl.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
                      "event_ms_per_step": round(a.elapsed_time(b) / args.config_steps, 4),
                      "dtype": wl.dtype, "T": wl.T, "d_model": wl.d_model, "d_ff": wl.d_ff, "E": wl.E,

@@ -584,25 +584,33 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, in
 }
 
 // dbias partials: block (x, y) adds dh[t][e] over token range y of S (fixed by T and
-// S only) for experts x*64 .. x*64+63, in token order, sixteen rows in flight;
-// part[y][e].  sum_slices_kernel then adds the S ranges in order, so the result is
-// the same on every call.
-__global__ __launch_bounds__(64) void bwd_bias_partial_kernel(const float* __restrict__ dh, int ldh, int ntok,
-                                                              int E, float* __restrict__ part) {
-  const int e = blockIdx.x * 64 + threadIdx.x;
+// S only) for experts x*64 .. x*64+63.  The range is cut in four contiguous quarters,
+// one per wave, each added in token order with sixteen rows in flight, then the
+// quarters in order: part[y][e] = ((q0 + q1) + q2) + q3.  sum_slices_kernel then adds
+// the S ranges in order, so the result is the same on every call.
+__global__ __launch_bounds__(256) void bwd_bias_partial_kernel(const float* __restrict__ dh, int ldh, int ntok,
+                                                               int E, float* __restrict__ part) {
+  __shared__ float q[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
   const int y = blockIdx.y, S = gridDim.y;
-  if (e >= E) return;
   const int t0 = static_cast<int>(static_cast<int64_t>(y) * ntok / S);
   const int t1 = static_cast<int>(static_cast<int64_t>(y + 1) * ntok / S);
+  const int a = t0 + static_cast<int>(static_cast<int64_t>(wave) * (t1 - t0) / 4);
+  const int z = t0 + static_cast<int>(static_cast<int64_t>(wave + 1) * (t1 - t0) / 4);
   float acc = 0.f;
-  for (int t = t0; t < t1; t += 16) {
-    float v[16];
+  if (e < E) {
+    for (int t = a; t < z; t += 16) {
+      float v[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = t + j < t1 ? dh[static_cast<int64_t>(t + j) * ldh + e] : 0.f;
+      for (int j = 0; j < 16; ++j) v[j] = t + j < z ? dh[static_cast<int64_t>(t + j) * ldh + e] : 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc += v[j];
+      for (int j = 0; j < 16; ++j) acc += v[j];
+    }
   }
-  part[static_cast<int64_t>(y) * E + e] = acc;
+  q[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && e < E) part[static_cast<int64_t>(y) * E + e] = ((q[0][lane] + q[1][lane]) + q[2][lane]) + q[3][lane];
 }
 
 // ---------------------------------------------------------------------------
@@ -806,7 +814,7 @@ static hipError_t backward_typed(const Plan& p, const BwdArgs& a, hipStream_t s)
       // the dw_r partial buffer, free again once dw_r is summed (stream order), then
       // the ranges added in order
       const int SB = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kBwdSplit, T_)));
-      hipLaunchKernelGGL(bwd_bias_partial_kernel, dim3((p.E + 63) / 64, SB), dim3(64), 0, s, a.dh, p.Epad,
+      hipLaunchKernelGGL(bwd_bias_partial_kernel, dim3((p.E + 63) / 64, SB), dim3(256), 0, s, a.dh, p.Epad,
                          T_, p.E, a.dwr_part);
       hipLaunchKernelGGL(sum_slices_kernel, dim3((p.E + 255) / 256), dim3(256), 0, s, a.dwr_part,
                          int64_t(p.E), SB, a.dbias);
