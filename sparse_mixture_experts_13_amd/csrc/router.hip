@@ -14,7 +14,12 @@
 // bf16 planes hi + mid + lo that sum to it exactly, so every product is exact;
 // when the weight is bf16-exact (mid = lo = 0, detected on the device) only the
 // hi plane is used.  Weight and token rows stream through an LDS stage ring fed
-// by direct global->LDS loads; the logits tile then goes to LDS, and sixteen
+// by direct global->LDS loads.  Eight waves per block: four only issue those
+// loads and wait for them, four only read fragments and run the MFMAs, so a load
+// issue held back by the memory pipeline never stalls the matrix pipe (with one
+// wave per SIMD doing both, a stage cost the sum of its load, LDS and MFMA times:
+// large-layer router and weight split 60 -> 47 us, Switch-Base 13.0 -> 11.2 us,
+// X-MoE 18.5 -> 14.8 us).  The logits tile then goes to LDS, and sixteen
 // lanes (one DPP row) rank each token by (logit, then lower index) with
 // cross-lane DPP moves.  The block's
 // expert histogram is built in LDS for the dispatch scan.  float32 tokens use a
@@ -135,8 +140,9 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 // weight rows 0..Epad-1, then the block's TB token rows, 128 bytes each) lands
 // in an S-deep LDS ring through direct global->LDS loads issued S-1 stages
 // ahead; for a non-bf16-exact weight the stages run over the hi, mid and lo
-// planes in turn.  Wave w owns expert tiles w, w+4, ... (up to EW of them)
-// against every token tile: D = W_r . x^T with v_mfma_f32_32x32x16_bf16.
+// planes in turn.  Loader waves 4..7 issue the stage loads; MFMA wave w (0..3)
+// owns expert tiles w, w+4, ... (up to EW of them) against every token tile:
+// D = W_r . x^T with v_mfma_f32_32x32x16_bf16.  All eight waves rank the tokens.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int64_t router_ring_bytes(int Epad, int TB, int S) {
   return static_cast<int64_t>(S) * (Epad + TB) * 128;
@@ -146,9 +152,10 @@ __host__ __device__ inline int64_t router_lg_bytes(int TB, int Epad) {
 }
 
 // Rank the tokens of a block from the logits tile lg [TB][ld] in LDS (both
-// routers).  Sixteen lanes share a token (a wave ranks four tokens at a time);
-// lane `sub` holds experts sub, sub+16, ...  Choices order by (logit desc, expert asc).
-template <int NV>
+// routers), NWV waves.  Sixteen lanes share a token (a wave ranks four tokens at a
+// time); lane `sub` holds experts sub, sub+16, ...  Choices order by (logit desc,
+// expert asc).
+template <int NV, int NWV>
 __device__ __forceinline__ void topk_epilogue16(const float* lg, int ld, int TB, int tok0, int ntok, int E, int k,
                                 const float* __restrict__ bias, int32_t* __restrict__ expert_idx,
                                 float* __restrict__ gate, int* hl, int ldh, int wave, int lane,
@@ -164,7 +171,7 @@ __device__ __forceinline__ void topk_epilogue16(const float* lg, int ld, int TB,
     bv[i] = bias && sub + 16 * i < E ? bias[sub + 16 * i] : 0.f;
   }
   constexpr float kLog2e = 1.4426950408889634f;
-  for (int base = 0; base < TB; base += 16) {
+  for (int base = 0; base < TB; base += 4 * NWV) {
     const int t = base + wave * 4 + grp;
     const bool valid = t < ntok;
     // every read is inside the tile (t < TB rows, e < Epad <= ld columns); the
@@ -240,13 +247,17 @@ __device__ __forceinline__ void topk_epilogue16(const float* lg, int ld, int TB,
       }
     }
     __syncthreads();
-    for (int e = wave * kWave + lane; e < E; e += 4 * kWave)
-      psum[e] = ((red[e] + red[ldh + e]) + red[2 * ldh + e]) + red[3 * ldh + e];
+    for (int e = wave * kWave + lane; e < E; e += NWV * kWave) {
+      float s = red[e];  // the waves' rows in wave order
+#pragma unroll
+      for (int w = 1; w < NWV; ++w) s += red[w * ldh + e];
+      psum[e] = s;
+    }
   }
 }
 
 template <int TT, int EW, int S>
-__global__ __launch_bounds__(256) void router_bf16_kernel(
+__global__ __launch_bounds__(512) void router_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, const int* __restrict__ flags,
     const float* __restrict__ bias, int T, int d, int E, int Epad, int k,
     int32_t* __restrict__ expert_idx, float* __restrict__ gate, int* __restrict__ hist, int NB,
@@ -254,18 +265,19 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   constexpr int TB = 32 * TT;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..3 MFMA, 4..7 loads
+  const int qw = wave & 3;
   const int half = lane >> 5, fr = lane & 31;
   const int b = blockIdx.x;
   const int tok0 = b * TB;
   const int ntok = min(TB, T - tok0);
   const int n_et = Epad / 32;
   const int rows = Epad + TB;
-  const int R = rows / 32;  // direct-to-LDS instructions per thread per stage
+  const int R = rows / 32;  // direct-to-LDS instructions per loader wave per stage
   const int64_t STAGE = static_cast<int64_t>(rows) * 128;
   const int64_t body = max(router_ring_bytes(Epad, TB, S), router_lg_bytes(TB, Epad));
   int* hl = reinterpret_cast<int*>(smem + body);  // [k][Epad]
-  for (int i = tid; i < k * Epad; i += 256) hl[i] = 0;
+  for (int i = tid; i < k * Epad; i += 512) hl[i] = 0;
 
   // the split kernel's flags, one per lane in a single vector load, then a wave
   // vote (one memory latency)
@@ -275,112 +287,123 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   const int total = (any ? 3 : 1) * KS;
   const int64_t plane_elems = static_cast<int64_t>(Epad) * d;
 
-  // Loads of one stage: this wave's instructions q (rows (4 q + wave) * 8 .. + 7,
-  // lane row row_q = ... + lane / 8) for q < R; RMAX bounds R at compile time so the
-  // issue loop unrolls, and each lane's row offsets are computed once: a stage only
-  // adds its k offset (and the plane offset).
-  constexpr int RMAX = 4 * EW + TT;
-  int64_t roff[RMAX];  // element offset of this lane's 16-byte chunk at k = 0
-  bool rw[RMAX];       // weight row (else token row)
-#pragma unroll
-  for (int q = 0; q < RMAX; ++q) {
-    const int rbase = (q * 4 + wave) * 8;
-    const int row = rbase + (lane >> 3);
-    const int c = (lane & 7) ^ lds_swz(row);
-    rw[q] = rbase < Epad;
-    if (rw[q]) roff[q] = static_cast<int64_t>(row) * d + c * 8;
-    else roff[q] = static_cast<int64_t>(min(tok0 + row - Epad, T - 1)) * d + c * 8;
-  }
-  // (the lambda below reads the arrays through pointers: capturing an array whose
-  // size depends on the template arguments leaves the kernel uninstantiated on the host)
-  const int64_t* roffp = roff;
-  const bool* rwp = rw;
-  // Blocks start their k loop at different offsets so that they do not all
-  // read the same router-weight rows at the same moment (hot L2 channels).
-  const int rot = b % KS;
-  auto issue = [&](int st, int slot) {
-    const int p = st / KS;
-    int ks = st - p * KS + rot;
-    ks = ks >= KS ? ks - KS : ks;
-    const bf16_t* wp = planes + p * plane_elems + ks * 64;
-    const bf16_t* xp = x + ks * 64;
-    unsigned char* base = smem + slot * STAGE + wave * 1024;
-#pragma unroll
-    for (int q = 0; q < RMAX; ++q)
-      if (q < R)
-        __builtin_amdgcn_global_load_lds((rwp[q] ? wp : xp) + roffp[q], (lds_void*)(base + q * 4096), 16, 0, 0);
-  };
-
   floatx16 acc[EW][TT];
+  if (wave >= 4) {
+    // Loader waves.  Instruction q of loader wave qw covers rows (4 q + qw) * 8 ..
+    // + 7 (lane row (4 q + qw) * 8 + lane / 8) for q < R; RMAX bounds R at compile
+    // time so the issue loop unrolls, and each lane's row offsets are computed
+    // once: a stage only adds its k offset (and the plane offset).
+    constexpr int RMAX = 4 * EW + TT;
+    int64_t roff[RMAX];  // element offset of this lane's 16-byte chunk at k = 0
+    bool rw[RMAX];       // weight row (else token row)
 #pragma unroll
-  for (int u = 0; u < EW; ++u)
+    for (int q = 0; q < RMAX; ++q) {
+      const int rbase = (q * 4 + qw) * 8;
+      const int row = rbase + (lane >> 3);
+      const int c = (lane & 7) ^ lds_swz(row);
+      rw[q] = rbase < Epad;
+      if (rw[q]) roff[q] = static_cast<int64_t>(row) * d + c * 8;
+      else roff[q] = static_cast<int64_t>(min(tok0 + row - Epad, T - 1)) * d + c * 8;
+    }
+    // (the lambda below reads the arrays through pointers: capturing an array whose
+    // size depends on the template arguments leaves the kernel uninstantiated on the host)
+    const int64_t* roffp = roff;
+    const bool* rwp = rw;
+    // Blocks start their k loop at different offsets so that they do not all
+    // read the same router-weight rows at the same moment (hot L2 channels).
+    const int rot = b % KS;
+    auto issue = [&](int st, int slot) {
+      const int p = st / KS;
+      int ks = st - p * KS + rot;
+      ks = ks >= KS ? ks - KS : ks;
+      const bf16_t* wp = planes + p * plane_elems + ks * 64;
+      const bf16_t* xp = x + ks * 64;
+      unsigned char* base = smem + slot * STAGE + qw * 1024;
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+      for (int q = 0; q < RMAX; ++q)
+        if (q < R)
+          __builtin_amdgcn_global_load_lds((rwp[q] ? wp : xp) + roffp[q], (lds_void*)(base + q * 4096), 16, 0, 0);
+    };
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[u][tt][r] = 0.f;
-
+    for (int i = 0; i < S - 1; ++i)
+      if (i < total) issue(i, i);
+    // stage st has landed (this wave's share of it) -> barrier -> the slot of stage
+    // st - 1, which every MFMA wave has read by now, takes stage st + S - 1
+    for (int st = 0; st < total; ++st) {
+      wait_vmcnt_dyn(total - 1 - st >= S - 2 ? (S - 2) * R : 0);
+      ring_barrier();
+      if (st + S - 1 < total) issue(st + S - 1, (st + S - 1) % S);
+    }
+  } else {
+    // MFMA waves: wave w owns expert tiles w, w+4, ... (up to EW of them) against
+    // every token tile; the fragments of sub-step j + 1 are read while sub-step j's
+    // MFMAs run.  A wave past the last expert tile multiplies a copy of it (its
+    // fragments are read clamped) and drops the result at the write-out: a branch
+    // around the MFMAs moved every accumulator between AGPRs and VGPRs.
 #pragma unroll
-  for (int i = 0; i < S - 1; ++i)
-    if (i < total) issue(i, i);
-  for (int st = 0; st < total; ++st) {
-    wait_vmcnt_dyn(total - 1 - st >= S - 2 ? (S - 2) * R : 0);
-    ring_barrier();
-    if (st + S - 1 < total) issue(st + S - 1, (st + S - 1) % S);
-    const unsigned char* sb = smem + (st % S) * STAGE;
-    // every fragment of the stage first (one LDS latency), then the MFMAs
-    bf16x8 bq[4][TT], a[4][EW];
+    for (int u = 0; u < EW; ++u)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = 2 * j + half;
+      for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        const int row = Epad + tt * 32 + fr;
-        bq[j][tt] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
-      }
+        for (int r = 0; r < 16; ++r) acc[u][tt][r] = 0.f;
+    for (int st = 0; st < total; ++st) {
+      ring_barrier();
+      const unsigned char* sb = smem + (st % S) * STAGE;
+      bf16x8 bq[2][TT], a[2][EW];
+      auto frag = [&](int j, int buf) {
+        const int c = 2 * j + half;
 #pragma unroll
-      for (int u = 0; u < EW; ++u) {
-        const int row = min(wave + 4 * u, n_et - 1) * 32 + fr;
-        a[j][u] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
+        for (int tt = 0; tt < TT; ++tt) {
+          const int row = Epad + tt * 32 + fr;
+          bq[buf][tt] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
+        }
+#pragma unroll
+        for (int u = 0; u < EW; ++u) {
+          const int row = min(wave + 4 * u, n_et - 1) * 32 + fr;
+          a[buf][u] = *reinterpret_cast<const bf16x8*>(sb + row * 128 + 16 * (c ^ lds_swz(row)));
+        }
+      };
+      frag(0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j + 1 < 4) frag(j + 1, (j + 1) & 1);
+#pragma unroll
+        for (int u = 0; u < EW; ++u)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+            acc[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 1][u], bq[j & 1][tt], acc[u][tt], 0, 0, 0);
       }
     }
-    // unconditional: a wave past the last expert tile multiplies a copy of it (its
-    // fragments are read clamped) and drops the result at the write-out; a branch
-    // here moved every accumulator between AGPRs and VGPRs around each MFMA
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int u = 0; u < EW; ++u)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-          acc[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][u], bq[j][tt], acc[u][tt], 0, 0, 0);
   }
-  __syncthreads();  // ring reads done before the logits tile overwrites it
+  __syncthreads();  // ring reads and loads done before the logits tile overwrites it
 
   // D[i][j] of a 32x32 tile: lane holds column j = lane % 32 (token) and rows
   // i = 8*(r/4) + 4*(lane/32) + r%4 (experts) of accumulator element r.
   float* lg = reinterpret_cast<float*>(smem);
   const int ld = Epad + 4;
+  if (wave < 4) {
 #pragma unroll
-  for (int u = 0; u < EW; ++u) {
-    const int et = wave + 4 * u;
-    if (et < n_et) {
+    for (int u = 0; u < EW; ++u) {
+      const int et = wave + 4 * u;
+      if (et < n_et) {
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int t = tt * 32 + fr;
-          const int e = et * 32 + 8 * g + 4 * half;
-          floatx4 v = {acc[u][tt][4 * g], acc[u][tt][4 * g + 1], acc[u][tt][4 * g + 2],
-                       acc[u][tt][4 * g + 3]};
-          *reinterpret_cast<floatx4*>(lg + t * ld + e) = v;
-        }
+          for (int g = 0; g < 4; ++g) {
+            const int t = tt * 32 + fr;
+            const int e = et * 32 + 8 * g + 4 * half;
+            floatx4 v = {acc[u][tt][4 * g], acc[u][tt][4 * g + 1], acc[u][tt][4 * g + 2],
+                         acc[u][tt][4 * g + 3]};
+            *reinterpret_cast<floatx4*>(lg + t * ld + e) = v;
+          }
+      }
     }
   }
   __syncthreads();
-  topk_epilogue16<8 * EW>(lg, ld, TB, tok0, ntok, E, k, bias, expert_idx, gate, hl, Epad, wave,
-                          lane, psum ? psum + static_cast<int64_t>(b) * Epad : nullptr, lg, hout, Epad);
+  topk_epilogue16<8 * EW, 8>(lg, ld, TB, tok0, ntok, E, k, bias, expert_idx, gate, hl, Epad, wave,
+                             lane, psum ? psum + static_cast<int64_t>(b) * Epad : nullptr, lg, hout, Epad);
   __syncthreads();
-  write_hist(hl, Epad, E, k, NB, b, hist, tid, 256);
+  write_hist(hl, Epad, E, k, NB, b, hist, tid, 512);
 }
 
 // ---------------------------------------------------------------------------
@@ -453,7 +476,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 #pragma unroll
   for (int j = 0; j < NACC; ++j) lg[t * ld + eg + 4 * j] = acc[j];
   __syncthreads();
-  topk_epilogue16<NACC / 4>(lg, ld, 64, tok0, ntok, E, k, bias, expert_idx, gate, hl, Ecap, wave,
+  topk_epilogue16<NACC / 4, 4>(lg, ld, 64, tok0, ntok, E, k, bias, expert_idx, gate, hl, Ecap, wave,
                             lane, psum ? psum + static_cast<int64_t>(b) * ldp : nullptr, lg, hout, ldp);
   __syncthreads();
   write_hist(hl, Ecap, E, k, NB, b, hist, tid, 256);
@@ -612,7 +635,7 @@ hipError_t launch_router_topk(const Plan& p, const void* x, const float* w_r, co
     const int64_t lds = std::max(router_ring_bytes(p.Epad, 32 * TT, S),                          \
                                  router_lg_bytes(32 * TT, p.Epad)) + 4LL * p.k * p.Epad;         \
     if ((err = set_lds(router_bf16_kernel<TT, EW, S>, lds)) != hipSuccess) return err;           \
-    hipLaunchKernelGGL((router_bf16_kernel<TT, EW, S>), dim3(p.NB), dim3(256), lds, s, xb, planes, \
+    hipLaunchKernelGGL((router_bf16_kernel<TT, EW, S>), dim3(p.NB), dim3(512), lds, s, xb, planes, \
                        flags, bias, T, d, p.E, p.Epad, p.k, expert_idx, gate, hist, p.NB, psum,   \
                        logits);                                                                  \
   } while (0)
