@@ -506,6 +506,187 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Grouped GEMM with the activation rows resident in LDS, for capacity <= 64 and
+// a contraction K <= 768 (the Switch-Base up-projection): every expert's rows
+// fit one 64-row block, and each of its column tiles would otherwise re-read
+// them with every stage (a fifth of the ring's load stream at 256 weight rows
+// per stage).  A block takes a contiguous share of the (expert, 256-column
+// block) tiles of the non-empty experts, consecutive shares on one XCD; for each
+// run of tiles of one expert it loads that expert's 64 x K activations into LDS
+// once (clamped rows past the count), then streams only weight rows: stages of
+// 128 weight rows x 64 k (16 KB) through a 4-slot direct-to-LDS ring, three in
+// flight.  Stage 2i + h of a tile carries k-chunk i of its rows 128 h .. + 127;
+// waves 4 h .. 4 h + 3 (32 weight rows each, all 64 activation rows: two
+// 32 x 32 MFMA tiles) multiply it.  The ring drains at a change of expert (at
+// most a couple of times per block).  Outputs, epilogue and GLU row order are
+// those of the ring kernel above.  In a memory-traffic emulation of the
+// Switch-Base up-projection (loads only, cold weights) this stream takes 95 us
+// against 105 us for the ring's 40 KB stages.
+// ---------------------------------------------------------------------------
+constexpr int kResRing = 4;                 // ring slots
+constexpr int kResStage = 128 * 128;        // 128 weight rows x 128 bytes
+constexpr int kResMaxK = 768;               // resident activations: 64 rows x K bf16 <= 96 KB
+__host__ __device__ constexpr int ffn_res_lds_bytes(int K) { return kResRing * kResStage + (K / 64) * 8192; }
+
+template <int ACT, bool GLU>
+__global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restrict__ A,
+                                                           const bf16_t* __restrict__ W,
+                                                           bf16_t* __restrict__ out,
+                                                           const int32_t* __restrict__ count,
+                                                           int E, int64_t C, int N, int K) {
+  constexpr int S = kResRing, BN = 256, CPR = 8;
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* ares = smem + S * kResStage;  // [K / 64 chunks][64 rows][128 bytes]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, fr = lane & 31;
+  const int KS = K / 64;
+  const int n_nb = (N + BN - 1) / BN;
+  auto rows_of = [&](int e) {
+    int64_t c = count[e];
+    return static_cast<int>(c < 0 ? 0 : (c > C ? C : c));
+  };
+  // the non-empty experts as a bit mask (E <= 512), the same in every wave
+  uint64_t nz[kMaxE / 64];
+  int nne = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxE / 64; ++i) {
+    const int e = i * 64 + lane;
+    nz[i] = __ballot(e < E && rows_of(e) > 0);
+    nne += __popcll(nz[i]);
+  }
+  const int V = nne * n_nb;
+  const int G = gridDim.x;
+  const int g = xcd_major_id(blockIdx.x, G);
+  const int v0 = static_cast<int>(static_cast<int64_t>(g) * V / G);
+  const int v1 = static_cast<int>(static_cast<int64_t>(g + 1) * V / G);
+  // the j-th non-empty expert (wave-uniform scalar search)
+  auto nth_expert = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < kMaxE / 64; ++i) {
+      uint64_t m = nz[i];
+      const int pc = __popcll(m);
+      if (j < pc) {
+        for (int r = 0; r < j; ++r) m &= m - 1;  // drop the j lowest set bits
+        return i * 64 + __builtin_ctzll(m);
+      }
+      j -= pc;
+    }
+    return E;
+  };
+
+  floatx16 acc[2];
+  for (int v = v0; v < v1;) {
+    const int j = v / n_nb;
+    const int e = nth_expert(j);
+    const int nb0 = v - j * n_nb;
+    const int nb1 = min(n_nb, nb0 + (v1 - v));
+    v += nb1 - nb0;
+    const int cnt = rows_of(e);
+    const int nst = (nb1 - nb0) * KS * 2;  // stages of this run of tiles
+    const bf16_t* We = W + static_cast<int64_t>(e) * N * K;
+    auto issue = [&](int st) {
+      const int nb = nb0 + (st >> 1) / KS, kc = (st >> 1) % KS, h = st & 1;
+      unsigned char* base = smem + (st % S) * kResStage;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int p = (wave * 2 + q) * 64 + lane;
+        const int row = p / CPR;
+        const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
+        int wr = min(nb * BN + h * 128 + row, N - 1);
+        if constexpr (GLU) wr = glu_row(wr, N >> 1);
+        const uint32_t off = static_cast<uint32_t>(wr) * K + kc * 64 + c * 8;
+        // non-temporal: each weight byte is read once per launch
+        __builtin_amdgcn_global_load_lds(We + off, (lds_void*)(base + (wave * 2 + q) * 1024), 16, 0, 2);
+      }
+    };
+    __syncthreads();  // the previous run is done with the ring and the resident rows
+    {
+      // resident activations: chunk kc of rows 0..63 at ares + kc * 8 KB, KS loads per wave
+      const bf16_t* Ae = A + static_cast<int64_t>(e) * C * K;
+      for (int q = 0; q < KS; ++q) {
+        const int p = (wave * KS + q) * 64 + lane;  // 16-byte chunk p of [KS][64][8]
+        const int kc = p >> 9, row = (p >> 3) & 63;
+        const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
+        const uint32_t off = static_cast<uint32_t>(min(row, cnt - 1)) * K + kc * 64 + c * 8;
+        __builtin_amdgcn_global_load_lds(Ae + off, (lds_void*)(ares + (wave * KS + q) * 1024), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i)
+      if (i < nst) issue(i);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+    const int wh = wave >> 2;                 // the half of the tile's rows this wave multiplies
+    const int wrow = (wave & 3) * 32 + fr;    // its fragment row within a stage
+    for (int st = 0; st < nst; ++st) {
+      // this wave's loads of stage st (and, before the first, of the resident rows)
+      if (nst - 1 - st >= S - 2) wait_vmcnt<(S - 2) * 2>();
+      else wait_vmcnt<0>();
+      ring_barrier();
+      if (st + S - 1 < nst) issue(st + S - 1);
+      const int kc = (st >> 1) % KS;
+      if ((st & 1) == wh) {
+        const unsigned char* sw = smem + (st % S) * kResStage;
+        const unsigned char* sa = ares + kc * 8192;
+        bf16x8 fa[4], fb[4][2];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int c = 2 * jj + half;
+          fa[jj] = *reinterpret_cast<const bf16x8*>(sw + wrow * 128 + 16 * (c ^ lds_swz_n<CPR>(wrow)));
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int row = t * 32 + fr;
+            fb[jj][t] = *reinterpret_cast<const bf16x8*>(sa + row * 128 + 16 * (c ^ lds_swz_n<CPR>(row)));
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[jj], fb[jj][t], acc[t], 0, 0, 0);
+      }
+      if ((st & 1) == 1 && kc == KS - 1) {
+        // tile done: D[n][m], lane holds m = lane % 32 and four consecutive n per group
+        const int nt0 = (nb0 + (st >> 1) / KS) * BN + wave * 32;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int m = t * 32 + fr;
+          if (m < cnt && nt0 < N) {
+            if constexpr (GLU) {
+              bf16_t* orow = out + (static_cast<int64_t>(e) * C + m) * (N >> 1);
+#pragma unroll
+              for (int q = 0; q < 2; ++q) {
+                float hv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) hv[u] = apply_act<ACT>(acc[t][4 * q + u]) * acc[t][4 * q + 8 + u];
+                uint2 val;
+                val.x = pack_bf16x2(hv[0], hv[1]);
+                val.y = pack_bf16x2(hv[2], hv[3]);
+                *reinterpret_cast<uint2*>(orow + (nt0 >> 1) + 8 * q + 4 * half) = val;
+              }
+            } else {
+              bf16_t* orow = out + (static_cast<int64_t>(e) * C + m) * N;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                uint2 val;
+                val.x = pack_bf16x2(apply_act<ACT>(acc[t][4 * q]), apply_act<ACT>(acc[t][4 * q + 1]));
+                val.y = pack_bf16x2(apply_act<ACT>(acc[t][4 * q + 2]), apply_act<ACT>(acc[t][4 * q + 3]));
+                *reinterpret_cast<uint2*>(orow + nt0 + 8 * q + 4 * half) = val;
+              }
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Ping-pong grouped GEMM for large capacities, where a tile re-reads its weight
 // rows for several row blocks and the MFMA pipe, not HBM, sets the pace.
 //
@@ -1186,6 +1367,22 @@ static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
   return hipGetLastError();
 }
 
+template <int ACT, bool GLU>
+static hipError_t run_res(int E, const bf16_t* A, const bf16_t* W, bf16_t* out, const int32_t* count,
+                          int64_t C, int N, int K, hipStream_t s) {
+  auto kern = ffn_res_bf16_kernel<ACT, GLU>;
+  const int lds = ffn_res_lds_bytes(K);
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err != hipSuccess) return err;
+  const int64_t tiles = static_cast<int64_t>(E) * ((N + 255) / 256);
+  if (tiles == 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>(tiles, 256);  // one persistent block per CU
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), lds, s, A, W, out, count, E, C,
+                     N, K);
+  return hipGetLastError();
+}
+
 template <int TM, int TN, int R, int ACT, bool GLU, bool BT = false, int EPI = 0>
 static hipError_t run_pp(int E, const bf16_t* A, const bf16_t* W, bf16_t* out, const int32_t* count,
                          int64_t C, int N, int K, hipStream_t s, const bf16_t* aux = nullptr) {
@@ -1235,7 +1432,11 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // Tile shapes by capacity.  Capacity <= 160: one row block holds every token of
 // an expert, so the GEMM is bound by streaming the weights once: persistent
 // direct-to-LDS ring kernel (8 or 4 waves, 256 weight rows per tile, 3-stage
-// ring).  When 384-row weight tiles would cover N exactly with at most one tile
+// ring).  Capacity <= 64 with a contraction of at most 768 (the activation rows
+// of an expert fit LDS): the kernel with resident activation rows and a
+// weight-only ring (Switch-Base up-projection inside the forward: 124 us against
+// 132 us for the ring's 40 KB stages, kernel trace of the same steps).  When
+// 384-row weight tiles would cover N exactly with at most one tile
 // per CU, 192-row tiles (two per CU, 4 waves, a 4-stage ring of 32 KB stages)
 // balance the CUs and keep three stages of a cold weight stream in flight
 // (Switch-Base down-projection inside the forward: 128-130 us, against 137 us
@@ -1267,6 +1468,8 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
     return run_pp<2, 4, 3, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (pp_ok && p.C > 160 && K >= 2048) return run_pp<4, 2, 4, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C > 160) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C <= 64 && K <= kResMaxK && p.E <= kMaxE)
+    return run_res<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
     return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
