@@ -514,19 +514,29 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
 // block) tiles of the non-empty experts, consecutive shares on one XCD; for each
 // run of tiles of one expert it loads that expert's 64 x K activations into LDS
 // once (clamped rows past the count), then streams only weight rows: stages of
-// 128 weight rows x 64 k (16 KB) through a 4-slot direct-to-LDS ring, three in
-// flight.  Stage 2i + h of a tile carries k-chunk i of its rows 128 h .. + 127;
-// waves 4 h .. 4 h + 3 (32 weight rows each, all 64 activation rows: two
-// 32 x 32 MFMA tiles) multiply it.  The ring drains at a change of expert (at
-// most a couple of times per block).  Outputs, epilogue and GLU row order are
-// those of the ring kernel above.  In a memory-traffic emulation of the
-// Switch-Base up-projection (loads only, cold weights) this stream takes 95 us
-// against 105 us for the ring's 40 KB stages.
+// 128 weight rows x 64 k (16 KB) through a 3-slot direct-to-LDS ring.  Stage
+// 2i + h of a tile carries k-chunk i of its rows 128 h .. + 127; waves 4 h ..
+// 4 h + 3 (32 weight rows each, all 64 activation rows: two 32 x 32 MFMA tiles)
+// multiply it.  The ring drains at a change of expert (at most a couple of
+// times per block).  In a memory-traffic emulation of the Switch-Base
+// up-projection (loads only, cold weights) this stream takes 95 us against
+// 105 us for the ring's 40 KB stages.
+// Output rows leave through a 32-row LDS staging tile as whole 512-byte row
+// segments with non-temporal stores: the hidden rows reach memory during this
+// kernel, where 8-byte stores left partly written lines in the caches whose
+// write-back then slowed the down-projection (Switch-Base, kernel traces of the
+// same forward steps: up 122 -> 114 us, down 129 -> 115 us, step 282 -> 262 us).
+// Waves 0-3 issue every load and waves 4-7 every output store, so no load wait
+// covers a store (gfx9 counts both in one counter).  GLU outputs (half-width
+// rows, two halves per unit) keep the direct 8-byte stores of the ring kernel.
 // ---------------------------------------------------------------------------
-constexpr int kResRing = 4;                 // ring slots
+constexpr int kResRing = 3;                 // ring slots
 constexpr int kResStage = 128 * 128;        // 128 weight rows x 128 bytes
 constexpr int kResMaxK = 768;               // resident activations: 64 rows x K bf16 <= 96 KB
-__host__ __device__ constexpr int ffn_res_lds_bytes(int K) { return kResRing * kResStage + (K / 64) * 8192; }
+constexpr int kResStg = 32 * 512;           // output staging: 32 rows x 256 columns bf16
+__host__ __device__ constexpr int ffn_res_lds_bytes(int K) {
+  return kResRing * kResStage + kResStg + (K / 64) * 8192;
+}
 
 template <int ACT, bool GLU>
 __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restrict__ A,
@@ -536,7 +546,8 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
                                                            int E, int64_t C, int N, int K) {
   constexpr int S = kResRing, BN = 256, CPR = 8;
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* ares = smem + S * kResStage;  // [K / 64 chunks][64 rows][128 bytes]
+  unsigned char* stg = smem + S * kResStage;          // [32 rows][512 bytes], chunk c at c ^ row
+  unsigned char* ares = stg + kResStg;                // [K / 64 chunks][64 rows][128 bytes]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, fr = lane & 31;
@@ -589,32 +600,32 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
       const int nb = nb0 + (st >> 1) / KS, kc = (st >> 1) % KS, h = st & 1;
       unsigned char* base = smem + (st % S) * kResStage;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int p = (wave * 2 + q) * 64 + lane;
+      for (int q = 0; q < 4; ++q) {  // loader waves 0-3
+        const int p = (wave * 4 + q) * 64 + lane;
         const int row = p / CPR;
         const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
         int wr = min(nb * BN + h * 128 + row, N - 1);
         if constexpr (GLU) wr = glu_row(wr, N >> 1);
         const uint32_t off = static_cast<uint32_t>(wr) * K + kc * 64 + c * 8;
         // non-temporal: each weight byte is read once per launch
-        __builtin_amdgcn_global_load_lds(We + off, (lds_void*)(base + (wave * 2 + q) * 1024), 16, 0, 2);
+        __builtin_amdgcn_global_load_lds(We + off, (lds_void*)(base + (wave * 4 + q) * 1024), 16, 0, 2);
       }
     };
     __syncthreads();  // the previous run is done with the ring and the resident rows
     {
       // resident activations: chunk kc of rows 0..63 at ares + kc * 8 KB, KS loads per wave
       const bf16_t* Ae = A + static_cast<int64_t>(e) * C * K;
-      for (int q = 0; q < KS; ++q) {
-        const int p = (wave * KS + q) * 64 + lane;  // 16-byte chunk p of [KS][64][8]
+      for (int q = 0; q < 2 * KS && wave < 4; ++q) {
+        const int p = (wave * 2 * KS + q) * 64 + lane;  // 16-byte chunk p of [KS][64][8]
         const int kc = p >> 9, row = (p >> 3) & 63;
         const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
         const uint32_t off = static_cast<uint32_t>(min(row, cnt - 1)) * K + kc * 64 + c * 8;
-        __builtin_amdgcn_global_load_lds(Ae + off, (lds_void*)(ares + (wave * KS + q) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(Ae + off, (lds_void*)(ares + (wave * 2 * KS + q) * 1024), 16, 0, 0);
       }
     }
 #pragma unroll
     for (int i = 0; i < S - 1; ++i)
-      if (i < nst) issue(i);
+      if (i < nst && wave < 4) issue(i);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -623,10 +634,12 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
     const int wrow = (wave & 3) * 32 + fr;    // its fragment row within a stage
     for (int st = 0; st < nst; ++st) {
       // this wave's loads of stage st (and, before the first, of the resident rows)
-      if (nst - 1 - st >= S - 2) wait_vmcnt<(S - 2) * 2>();
-      else wait_vmcnt<0>();
+      if (wave < 4) {  // loader waves; waves 4-7 issue only the output stores
+        if (nst - 1 - st >= S - 2) wait_vmcnt<(S - 2) * 4>();
+        else wait_vmcnt<0>();
+      }
       ring_barrier();
-      if (st + S - 1 < nst) issue(st + S - 1);
+      if (st + S - 1 < nst && wave < 4) issue(st + S - 1);
       const int kc = (st >> 1) % KS;
       if ((st & 1) == wh) {
         const unsigned char* sw = smem + (st % S) * kResStage;
@@ -650,12 +663,13 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
       }
       if ((st & 1) == 1 && kc == KS - 1) {
         // tile done: D[n][m], lane holds m = lane % 32 and four consecutive n per group
-        const int nt0 = (nb0 + (st >> 1) / KS) * BN + wave * 32;
+        const int n0t = (nb0 + (st >> 1) / KS) * BN;
+        const int nt0 = n0t + wave * 32;
+        if constexpr (GLU) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int m = t * 32 + fr;
-          if (m < cnt && nt0 < N) {
-            if constexpr (GLU) {
+          for (int t = 0; t < 2; ++t) {
+            const int m = t * 32 + fr;
+            if (m < cnt && nt0 < N) {
               bf16_t* orow = out + (static_cast<int64_t>(e) * C + m) * (N >> 1);
 #pragma unroll
               for (int q = 0; q < 2; ++q) {
@@ -667,19 +681,40 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
                 val.y = pack_bf16x2(hv[2], hv[3]);
                 *reinterpret_cast<uint2*>(orow + (nt0 >> 1) + 8 * q + 4 * half) = val;
               }
-            } else {
-              bf16_t* orow = out + (static_cast<int64_t>(e) * C + m) * N;
+            }
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                uint2 val;
-                val.x = pack_bf16x2(apply_act<ACT>(acc[t][4 * q]), apply_act<ACT>(acc[t][4 * q + 1]));
-                val.y = pack_bf16x2(apply_act<ACT>(acc[t][4 * q + 2]), apply_act<ACT>(acc[t][4 * q + 3]));
-                *reinterpret_cast<uint2*>(orow + nt0 + 8 * q + 4 * half) = val;
+            for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+          }
+        } else {
+          // two 32-row passes through the staging tile, then whole 512-byte row
+          // segments (four cache lines) per 32 threads, non-temporal: the hidden rows
+          // go to memory now instead of being written back during the next kernel
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int n = wave * 32 + 8 * q + 4 * half;  // column within the tile
+              uint2 val;
+              val.x = pack_bf16x2(apply_act<ACT>(acc[t][4 * q]), apply_act<ACT>(acc[t][4 * q + 1]));
+              val.y = pack_bf16x2(apply_act<ACT>(acc[t][4 * q + 2]), apply_act<ACT>(acc[t][4 * q + 3]));
+              *reinterpret_cast<uint2*>(stg + fr * 512 + (((n >> 3) ^ fr) << 4) + (n & 7) * 2) = val;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+            ring_barrier();
+            if (wave >= 4) {
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) {
+                const int q = (tid - 256) + 256 * ii;
+                const int ml = q >> 5, c = q & 31;
+                const int m = t * 32 + ml, n = n0t + c * 8;
+                if (m < cnt && n < N)
+                  __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + ml * 512 + ((c ^ ml) << 4)),
+                                              reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(e) * C + m) * N + n));
               }
             }
+            ring_barrier();  // staging reads done before it is written again
           }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
         }
       }
     }
@@ -1434,8 +1469,9 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // direct-to-LDS ring kernel (8 or 4 waves, 256 weight rows per tile, 3-stage
 // ring).  Capacity <= 64 with a contraction of at most 768 (the activation rows
 // of an expert fit LDS): the kernel with resident activation rows and a
-// weight-only ring (Switch-Base up-projection inside the forward: 124 us against
-// 132 us for the ring's 40 KB stages, kernel trace of the same steps).  When
+// weight-only ring, outputs through an LDS staging tile as whole rows (Switch-Base
+// up-projection inside the forward: 114 us against 132 us for the ring's 40 KB
+// stages, and the down-projection after it 115 against 129 us).  When
 // 384-row weight tiles would cover N exactly with at most one tile
 // per CU, 192-row tiles (two per CU, 4 waves, a 4-stage ring of 32 KB stages)
 // balance the CUs and keep three stages of a cold weight stream in flight
