@@ -232,9 +232,17 @@ def training_extras(args, wl, cfg, x, w_r, bias, gid, w1, w2, y, y2, ws, x_e, cn
     kern_us["backward"] = timed(lambda: moe.backward(cfg, x, w_r, bias, w1, w2, dy_t, dx_t, dwr_t, dbias_t,
                                                      dw1_t, dw2_t, ws, bws, stream), max(2, R // 2))
     nc_t = torch.empty(2, dtype=torch.float32, device=dev)
-    # SparseClip with clipping active (norm pass + in-place scale) and inactive (norm pass only)
-    kern_us["sparse_clip"] = timed(lambda: moe.sparse_clip(cfg, dwr_t, dbias_t, dw1_t, dw2_t, 1e-3, nc_t, bws,
-                                                           stream), max(2, R // 2))
+    # SparseClip with clipping active (norm pass + in-place scale) and inactive (norm pass only);
+    # each active call clips to a bound 0.7x the previous one, so that no call finds the
+    # gradients already inside its bound (a repeated bound leaves the second call with the
+    # norm the first produced, which may round to just below it: no scale pass)
+    bound = [1e-3]
+
+    def clip_active():
+        bound[0] *= 0.7
+        moe.sparse_clip(cfg, dwr_t, dbias_t, dw1_t, dw2_t, bound[0], nc_t, bws, stream)
+
+    kern_us["sparse_clip"] = timed(clip_active, max(2, R // 2))
     kern_us["sparse_clip_inactive"] = timed(lambda: moe.sparse_clip(cfg, dwr_t, dbias_t, dw1_t, dw2_t, 1e30, nc_t,
                                                                     bws, stream), max(2, R // 2))
     del dw1_t, dw2_t, bws

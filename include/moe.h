@@ -90,7 +90,11 @@ int64_t moe_capacity(const moe_config* cfg);
  * on an invalid configuration. */
 int64_t moe_workspace_bytes(const moe_config* cfg);
 
-/* Regions of the workspace that moe_forward fills, for inspection after the call. */
+/* Regions of the workspace that moe_forward fills, for inspection after the call.
+ * One exception: on bfloat16 layers with capacity <= 64, d_model <= 768 and
+ * E <= 512 the up-projection reads each slot's token row from x itself
+ * (through slot_token), and moe_forward leaves MOE_WS_X_E unwritten there
+ * (moe_dispatch always writes its x_e; moe_backward gathers the rows again). */
 typedef enum {
   MOE_WS_EXPERT_IDX = 0,   /* int32 [T, k]                                   */
   MOE_WS_GATE = 1,         /* float [T, k]                                   */
@@ -213,9 +217,9 @@ int moe_combine(const moe_config* cfg, const void* y_e, const int32_t* expert_id
                 const int32_t* slot, const float* gate, void* y, void* stream);
 
 /* The whole layer, steps 1-5, on one stream.  Same arguments and results as
- * the step-wise calls; every intermediate is left in `ws` at the offsets of
- * moe_workspace_offset.  Capacity comes from the configuration alone, so no
- * device-to-host copy happens anywhere. */
+ * the step-wise calls, bit for bit; every intermediate is left in `ws` at the
+ * offsets of moe_workspace_offset (x_e: see moe_ws_region).  Capacity comes
+ * from the configuration alone, so no device-to-host copy happens anywhere. */
 int moe_forward(const moe_config* cfg, const void* x, const float* w_r, const float* bias,
                 const int32_t* group_id, const void* w1, const void* w2, void* y, void* ws,
                 void* stream);
@@ -255,7 +259,9 @@ int64_t moe_backward_workspace_bytes(const moe_config* cfg);
  * the router gets no gradient (w_r, bias, dw_r, dbias are ignored).
  * Precondition: `ws` holds the results of moe_forward on the same cfg, x, w_r,
  * bias, w1 and w2 (routing, slots, x_e, hidden activations and y_e); the
- * router is run again here and rewrites identical values into `ws`.
+ * router is run again here and rewrites identical values into `ws`, and where
+ * moe_forward left x_e unwritten (see moe_ws_region) it is gathered here from
+ * x and slot_token.
  *   dy    [T, d_model] dtype: dL/dy
  *   dx    [T, d_model] dtype out: dL/dx (expert path plus router path)
  *   dw_r  [E, d_model] float32 out (learned routing): dL/dW_r

@@ -13,7 +13,9 @@
 //   3. per token: rank among the earlier tokens of its block with the same
 //      expert for the same choice, slot = offset + rank (dropped if >= C), then
 //      the token's row is copied once from x into every expert slot it holds
-//      (16-byte vector loads/stores).
+//      (16-byte vector loads/stores).  Without an x_e buffer the pass stops
+//      after the slots: the whole-layer call does that where the up-projection
+//      reads each slot's token row from x itself.
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -112,6 +114,7 @@ __global__ __launch_bounds__(256) void dispatch_slot_gather_kernel(
     dst_e[tl * k + c] = e;
     dst_s[tl * k + c] = s;
   }
+  if (x_e == nullptr) return;  // slots only (uniform over the block)
   __syncthreads();
   if (tid < kSlotTokens) {
     bool any = false;
@@ -152,6 +155,35 @@ __global__ __launch_bounds__(256) void dispatch_slot_gather_kernel(
       }
     }
   }
+}
+
+// The gathered rows alone, from slot_token (the backward after a whole-layer call
+// that left x_e unwritten): one wave per slot row, x_e[e, s] = x[slot_token[e, s]]
+// for s < expert_count[e], 16-byte vectors.
+__global__ __launch_bounds__(256) void gather_slots_kernel(const uint8_t* __restrict__ x,
+                                                           const int32_t* __restrict__ slot_token,
+                                                           const int32_t* __restrict__ expert_count,
+                                                           int64_t nrows, int64_t C, int64_t row_bytes,
+                                                           uint8_t* __restrict__ x_e) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= nrows) return;
+  const int64_t e = r / C, s = r - e * C;
+  if (s >= expert_count[e]) return;
+  const int64_t t = slot_token[r];
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + t * row_bytes);
+  u32x4* dst = reinterpret_cast<u32x4*>(x_e + r * row_bytes);
+  for (int64_t v = lane; v < row_bytes / 16; v += kWave) dst[v] = src[v];
+}
+
+hipError_t launch_gather_slots(const Plan& p, const void* x, const int32_t* slot_token,
+                               const int32_t* expert_count, void* x_e, hipStream_t s) {
+  const int64_t nrows = static_cast<int64_t>(p.E) * p.C;
+  if (nrows == 0 || p.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_slots_kernel, dim3(static_cast<unsigned>((nrows + 3) / 4)), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(x), slot_token, expert_count, nrows, p.C, p.d * p.elem,
+                     static_cast<uint8_t*>(x_e));
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch_hist(const Plan& p, const int32_t* expert_idx, void* ws, hipStream_t s) {

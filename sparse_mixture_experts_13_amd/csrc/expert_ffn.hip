@@ -529,6 +529,11 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
 // Waves 0-3 issue every load and waves 4-7 every output store, so no load wait
 // covers a store (gfx9 counts both in one counter).  GLU outputs (half-width
 // rows, two halves per unit) keep the direct 8-byte stores of the ring kernel.
+// With `tok` (the whole-layer call) A is the token rows x [T][K] and row s of
+// expert e is x[tok[e C + s]]: the resident load gathers the rows itself and
+// the dispatch writes no x_e.  The block loads the expert's 64 slot tokens with
+// one vector load, issues its first weight stages, then the row loads (each
+// lane's token from a cross-lane read).
 // ---------------------------------------------------------------------------
 constexpr int kResRing = 3;                 // ring slots
 constexpr int kResStage = 128 * 128;        // 128 weight rows x 128 bytes
@@ -543,7 +548,8 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
                                                            const bf16_t* __restrict__ W,
                                                            bf16_t* __restrict__ out,
                                                            const int32_t* __restrict__ count,
-                                                           int E, int64_t C, int N, int K) {
+                                                           int E, int64_t C, int N, int K,
+                                                           const int32_t* __restrict__ tok) {
   constexpr int S = kResRing, BN = 256, CPR = 8;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* stg = smem + S * kResStage;          // [32 rows][512 bytes], chunk c at c ^ row
@@ -612,8 +618,8 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
       }
     };
     __syncthreads();  // the previous run is done with the ring and the resident rows
-    {
-      // resident activations: chunk kc of rows 0..63 at ares + kc * 8 KB, KS loads per wave
+    // resident activations: chunk kc of rows 0..63 at ares + kc * 8 KB, 2 KS loads per wave
+    if (tok == nullptr) {
       const bf16_t* Ae = A + static_cast<int64_t>(e) * C * K;
       for (int q = 0; q < 2 * KS && wave < 4; ++q) {
         const int p = (wave * 2 * KS + q) * 64 + lane;  // 16-byte chunk p of [KS][64][8]
@@ -622,10 +628,26 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
         const uint32_t off = static_cast<uint32_t>(min(row, cnt - 1)) * K + kc * 64 + c * 8;
         __builtin_amdgcn_global_load_lds(Ae + off, (lds_void*)(ares + (wave * 2 * KS + q) * 1024), 16, 0, 0);
       }
-    }
 #pragma unroll
-    for (int i = 0; i < S - 1; ++i)
-      if (i < nst && wave < 4) issue(i);
+      for (int i = 0; i < S - 1; ++i)
+        if (i < nst && wave < 4) issue(i);
+    } else if (wave < 4) {
+      // lane l: the token of slot min(l, cnt - 1); the first weight stages go out
+      // while it arrives, the row loads after them (the main loop's first wait
+      // then drains every load of the wave)
+      const int trow = tok[static_cast<int64_t>(e) * C + min(lane, cnt - 1)];
+#pragma unroll
+      for (int i = 0; i < S - 1; ++i)
+        if (i < nst) issue(i);
+      for (int q = 0; q < 2 * KS; ++q) {
+        const int p = (wave * 2 * KS + q) * 64 + lane;
+        const int kc = p >> 9, row = (p >> 3) & 63;
+        const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
+        const int t = __shfl(trow, row, kWave);
+        const bf16_t* src = A + static_cast<int64_t>(t) * K + kc * 64 + c * 8;
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(ares + (wave * 2 * KS + q) * 1024), 16, 0, 0);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -635,7 +657,7 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
     for (int st = 0; st < nst; ++st) {
       // this wave's loads of stage st (and, before the first, of the resident rows)
       if (wave < 4) {  // loader waves; waves 4-7 issue only the output stores
-        if (nst - 1 - st >= S - 2) wait_vmcnt<(S - 2) * 4>();
+        if (nst - 1 - st >= S - 2 && (tok == nullptr || st > 0)) wait_vmcnt<(S - 2) * 4>();
         else wait_vmcnt<0>();
       }
       ring_barrier();
@@ -1404,7 +1426,7 @@ static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
 
 template <int ACT, bool GLU>
 static hipError_t run_res(int E, const bf16_t* A, const bf16_t* W, bf16_t* out, const int32_t* count,
-                          int64_t C, int N, int K, hipStream_t s) {
+                          int64_t C, int N, int K, hipStream_t s, const int32_t* tok = nullptr) {
   auto kern = ffn_res_bf16_kernel<ACT, GLU>;
   const int lds = ffn_res_lds_bytes(K);
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1414,7 +1436,7 @@ static hipError_t run_res(int E, const bf16_t* A, const bf16_t* W, bf16_t* out, 
   if (tiles == 0) return hipSuccess;
   const int64_t grid = std::min<int64_t>(tiles, 256);  // one persistent block per CU
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), lds, s, A, W, out, count, E, C,
-                     N, K);
+                     N, K, tok);
   return hipGetLastError();
 }
 
@@ -1493,6 +1515,17 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // ring kernels address inside one expert with 32-bit offsets; larger experts
 // take the LDS-tiled one.  N is the number of weight rows (2 d_ff for the GLU
 // up-projection).
+// The resident-activation kernel's shape conditions (N x K and C x K element
+// offsets in 32 bits, one 64-row block per expert, the rows of K fit in LDS).
+static bool res_ok(const Plan& p, int64_t N, int64_t K) {
+  const int64_t lim = int64_t(1) << 32;
+  return N * K < lim && p.C * K < lim && p.C <= 64 && K <= kResMaxK && p.E <= kMaxE;
+}
+
+bool up_reads_token_rows(const Plan& p) {
+  return p.dtype == 1 && p.C > 0 && p.T > 0 && res_ok(p, p.w1_rows(), p.d);
+}
+
 template <int ACT, bool GLU = false>
 static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf16_t* out,
                             const int32_t* count, int N, int K, hipStream_t s) {
@@ -1504,8 +1537,7 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
     return run_pp<2, 4, 3, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (pp_ok && p.C > 160 && K >= 2048) return run_pp<4, 2, 4, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C > 160) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C <= 64 && K <= kResMaxK && p.E <= kMaxE)
-    return run_res<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (res_ok(p, N, K)) return run_res<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
     return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
@@ -1599,6 +1631,26 @@ hipError_t launch_expert_down(const Plan& p, const void* hidden, const int32_t* 
                         static_cast<bf16_t*>(y_e), expert_count, d, f, s);
   return run_f32<2>(p.E, static_cast<const float*>(hidden), static_cast<const float*>(w2),
                     static_cast<float*>(y_e), expert_count, p.C, d, f, s);
+}
+
+hipError_t launch_expert_ffn_rows(const Plan& p, const void* x, const int32_t* slot_token,
+                                  const int32_t* expert_count, const void* w1, const void* w2,
+                                  void* y_e, void* ws, hipStream_t s) {
+  if (!up_reads_token_rows(p)) return hipErrorInvalidValue;
+  void* hidden = ws_at(ws, p.off_region[6]);
+  const bf16_t* xr = static_cast<const bf16_t*>(x);
+  const bf16_t* w = static_cast<const bf16_t*>(w1);
+  bf16_t* h = static_cast<bf16_t*>(hidden);
+  const int d = static_cast<int>(p.d), f = static_cast<int>(p.f);
+  hipError_t err;
+  if (p.glu)
+    err = p.act == 0 ? run_res<0, true>(p.E, xr, w, h, expert_count, p.C, 2 * f, d, s, slot_token)
+                     : run_res<1, true>(p.E, xr, w, h, expert_count, p.C, 2 * f, d, s, slot_token);
+  else
+    err = p.act == 0 ? run_res<0, false>(p.E, xr, w, h, expert_count, p.C, f, d, s, slot_token)
+                     : run_res<1, false>(p.E, xr, w, h, expert_count, p.C, f, d, s, slot_token);
+  if (err != hipSuccess) return err;
+  return launch_expert_down(p, hidden, expert_count, w2, y_e, s);
 }
 
 hipError_t launch_expert_ffn(const Plan& p, const void* x_e, const int32_t* expert_count,

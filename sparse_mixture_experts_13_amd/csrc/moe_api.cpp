@@ -404,9 +404,16 @@ int run_forward(const moe::Plan& p, const void* x, const float* w_r, const float
   MOE_CHECK(run_router(p, x, w_r, bias, group_id, expert_idx, gate, ws, s));
   // the router wrote the per-block histograms; dispatch starts at the scan
   MOE_HIP(moe::launch_dispatch_scan(p, count, slot_token, ws, s), "dispatch scan");
-  MOE_HIP(moe::launch_dispatch_slot_gather(p, x, expert_idx, slot, slot_token, x_e, ws, s),
-          "dispatch slots/gather");
-  MOE_HIP(moe::launch_expert_ffn(p, x_e, count, w1, w2, y_e, ws, s), "expert ffn");
+  if (moe::up_reads_token_rows(p)) {
+    // the up-projection gathers each slot's row from x itself: slots only, no x_e
+    MOE_HIP(moe::launch_dispatch_slot_gather(p, x, expert_idx, slot, slot_token, nullptr, ws, s),
+            "dispatch slots");
+    MOE_HIP(moe::launch_expert_ffn_rows(p, x, slot_token, count, w1, w2, y_e, ws, s), "expert ffn");
+  } else {
+    MOE_HIP(moe::launch_dispatch_slot_gather(p, x, expert_idx, slot, slot_token, x_e, ws, s),
+            "dispatch slots/gather");
+    MOE_HIP(moe::launch_expert_ffn(p, x_e, count, w1, w2, y_e, ws, s), "expert ffn");
+  }
   MOE_HIP(moe::launch_combine(p, y_e, expert_idx, slot, gate, y, s), "combine");
   return MOE_OK;
 }
@@ -499,6 +506,13 @@ int moe_backward(const moe_config* cfg, const void* x, const float* w_r, const f
   a.slot = reinterpret_cast<const int32_t*>(base + p.off_region[MOE_WS_SLOT]);
   a.count = reinterpret_cast<const int32_t*>(base + p.off_region[MOE_WS_EXPERT_COUNT]);
   a.x_e = base + p.off_region[MOE_WS_X_E];
+  if (moe::up_reads_token_rows(p)) {
+    // moe_forward left x_e unwritten (its up-projection read x[slot_token]): the
+    // weight gradient of the up-projection needs the gathered rows
+    MOE_HIP(moe::launch_gather_slots(p, x, reinterpret_cast<const int32_t*>(base + p.off_region[MOE_WS_SLOT_TOKEN]),
+                                     a.count, base + p.off_region[MOE_WS_X_E], static_cast<hipStream_t>(stream)),
+            "gather x_e");
+  }
   a.hidden = base + p.off_region[MOE_WS_HIDDEN];
   a.y_e = base + p.off_region[MOE_WS_Y_E];
   a.ws = ws;

@@ -47,15 +47,28 @@ hipError_t launch_router_rre(const Plan& p, const int32_t* group_id, int32_t* ex
 hipError_t launch_dispatch_hist(const Plan& p, const int32_t* expert_idx, void* ws, hipStream_t s);
 hipError_t launch_dispatch_scan(const Plan& p, int32_t* expert_count, int32_t* slot_token, void* ws,
                                 hipStream_t s);
+// x_e null: slots only (slot, slot_token), no row copy
 hipError_t launch_dispatch_slot_gather(const Plan& p, const void* x, const int32_t* expert_idx,
                                        int32_t* slot, int32_t* slot_token, void* x_e, void* ws,
                                        hipStream_t s);
+// x_e[e, s] = x[slot_token[e, s]] for s < expert_count[e]
+hipError_t launch_gather_slots(const Plan& p, const void* x, const int32_t* slot_token,
+                               const int32_t* expert_count, void* x_e, hipStream_t s);
 
 // expert_ffn.hip
 hipError_t launch_expert_ffn(const Plan& p, const void* x_e, const int32_t* expert_count,
                              const void* w1, const void* w2, void* y_e, void* ws, hipStream_t s);
 hipError_t launch_expert_up(const Plan& p, const void* x_e, const int32_t* expert_count,
                             const void* w1, void* hidden, hipStream_t s);
+// True where the up-projection can read each slot's activation row from the
+// token rows x through slot_token instead of from x_e (the resident-activation
+// GEMM: bf16, capacity <= 64, d_model <= 768, E <= 512).
+bool up_reads_token_rows(const Plan& p);
+// The expert FFN of launch_expert_ffn with the up-projection reading x[slot_token]
+// (only where up_reads_token_rows holds; hipErrorInvalidValue elsewhere).
+hipError_t launch_expert_ffn_rows(const Plan& p, const void* x, const int32_t* slot_token,
+                                  const int32_t* expert_count, const void* w1, const void* w2,
+                                  void* y_e, void* ws, hipStream_t s);
 // Fused FFN (bf16, capacity <= 64): column groups per expert, 0 if not applicable:
 // bf16, capacity <= 64, d_ff a multiple of the 128-column hidden chunk, and d_model a
 // multiple of 384 split into column groups of 384 (two 192-column accumulator tiles

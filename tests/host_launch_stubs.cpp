@@ -21,8 +21,14 @@ hipError_t launch_dispatch_hist(const Plan&, const int32_t*, void*, hipStream_t)
 hipError_t launch_dispatch_scan(const Plan&, int32_t*, int32_t*, void*, hipStream_t) { return no_device(); }
 hipError_t launch_dispatch_slot_gather(const Plan&, const void*, const int32_t*, int32_t*, int32_t*, void*,
                                        void*, hipStream_t) { return no_device(); }
+hipError_t launch_gather_slots(const Plan&, const void*, const int32_t*, const int32_t*, void*, hipStream_t) {
+  return no_device();
+}
 hipError_t launch_expert_ffn(const Plan&, const void*, const int32_t*, const void*, const void*, void*,
                              void*, hipStream_t) { return no_device(); }
+bool up_reads_token_rows(const Plan&) { return false; }
+hipError_t launch_expert_ffn_rows(const Plan&, const void*, const int32_t*, const int32_t*, const void*,
+                                  const void*, void*, void*, hipStream_t) { return no_device(); }
 hipError_t launch_expert_up(const Plan&, const void*, const int32_t*, const void*, void*, hipStream_t) {
   return no_device();
 }
