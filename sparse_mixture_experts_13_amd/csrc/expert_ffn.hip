@@ -231,11 +231,17 @@ __host__ __device__ constexpr int ffn_ring_lds_bytes() {
   return S * (WN * TN * 32 + WM * TM * 32) * BK * 2 + (kMaxE + 1) * 4;
 }
 
-template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT, bool GLU>
+// PAIR: the unit of work is two adjacent column tiles of one row block (column
+// blocks 2 u and 2 u + 1), multiplied together: the stages alternate between
+// their weight rows at each k-chunk (k-chunk i of half 0, then of half 1), each
+// stage carrying the row block's k-chunk i, so the second copy of every
+// activation chunk is read while the first is still in L2.
+template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT, bool GLU, bool PAIR = false>
 __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
     const int32_t* __restrict__ count, int E, int64_t C, int N, int K) {
   constexpr int NW = WM * WN;
+  constexpr int NH = PAIR ? 2 : 1;  // column tiles per unit
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int RB = BK * 2;         // LDS row bytes
   constexpr int CPR = BK / 8;        // 16-byte chunks per row
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave - (wave / WN) * WN;
   const int half = lane >> 5, fr = lane & 31;
-  const int n_nb = (N + BN - 1) / BN;
+  const int n_nb = (N + BN * NH - 1) / (BN * NH);  // column units (PAIR: N % (2 BN) == 0)
   const int KS = K / BK;
 
   auto rows_of = [&](int e) {
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
     vs = (G - x + NX - 1) / NX;  // blocks in this group
   }
   const int ntile = v0 < v1 ? (v1 - v0 + vs - 1) / vs : 0;
-  const int total = ntile * KS;
+  const int total = ntile * KS * NH;
   if (total == 0) return;
 
   // a tile cursor: expert, row block, column block of linear non-empty tile v;
@@ -358,7 +364,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
   lc.e = 0;
   seek(lc, v0);
   cc = lc;
-  int lk = 0;
+  int lk = 0, lh = 0;  // loader: k-chunk and column half of the stage it issues next
   // Loads use a block-uniform per-expert base plus 32-bit lane offsets.
   // issue_one(slot, q) issues the q-th of the PER_STAGE direct-to-LDS
   // instructions of the loader's current stage; advance() moves to the next.
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
       const int p = (wave * WL + q) * 64 + lane;
       const int row = p / CPR;
       const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
-      int wr = min(lc.nb * BN + row, N - 1);
+      int wr = min((lc.nb * NH + lh) * BN + row, N - 1);
       if constexpr (GLU) wr = glu_row(wr, N >> 1);
       const uint32_t off = static_cast<uint32_t>(wr) * K + lk * BK + c * 8;
       // non-temporal when each weight tile is read by one row block only
@@ -387,6 +393,8 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
     }
   };
   auto advance = [&]() {
+    if (PAIR && ++lh < NH) return;
+    lh = 0;
     if (++lk == KS) {
       lk = 0;
       step(lc);
@@ -398,14 +406,16 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
     advance();
   };
 
-  floatx16 acc[TN][TM];
+  floatx16 acc[NH][TN][TM];
   auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int t = 0; t < TM; ++t)
+      for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.f;
+        for (int t = 0; t < TM; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[h][i][t][r] = 0.f;
   };
 #pragma unroll
   for (int i = 0; i < S - 1; ++i)
@@ -413,89 +423,95 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
   int s = 0;  // stage index over the block's whole sequence
   for (int it = 0; it < ntile; ++it) {
     zero_acc();
-    for (int kk = 0; kk < KS; ++kk, ++s) {
-      if (total - 1 - s >= S - 2) wait_vmcnt<(S - 2) * PER_STAGE>();
-      else wait_vmcnt<0>();
-      ring_barrier();
-      // the next stage's loads are spread between this stage's MFMAs, so that
-      // issuing them does not stall the wave ahead of its math
-      const bool pf = s + S - 1 < total;
-      const int pslot = (s + S - 1) % S;
-      const unsigned char* sw = smem + (s % S) * STAGE;
-      const unsigned char* sa = sw + BN * RB;
-      // fragments of sub-step j + 1 load while sub-step j's MFMAs run
-      bf16x8 fa[2][TN], fb[2][TM];
-      auto load_frags = [&](int j, int buf) {
-        const int c = 2 * j + half;
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int t = 0; t < TM; ++t) {
-          const int row = (wm * TM + t) * 32 + fr;
-          fb[buf][t] = *reinterpret_cast<const bf16x8*>(sa + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
-        }
-#pragma unroll
-        for (int i = 0; i < TN; ++i) {
-          const int row = (wn * TN + i) * 32 + fr;
-          fa[buf][i] = *reinterpret_cast<const bf16x8*>(sw + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
-        }
-      };
-      constexpr int NJ = BK / 16;           // MFMA sub-steps per stage
-      constexpr int MT = NJ * TN * TM;      // MFMAs per stage
-      load_frags(0, 0);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if (j + 1 < NJ) load_frags(j + 1, (j + 1) & 1);
-#pragma unroll
-        for (int i = 0; i < TN; ++i)
+      for (int hh = 0; hh < NH; ++hh, ++s) {
+        if (total - 1 - s >= S - 2) wait_vmcnt<(S - 2) * PER_STAGE>();
+        else wait_vmcnt<0>();
+        ring_barrier();
+        // the next stage's loads are spread between this stage's MFMAs, so that
+        // issuing them does not stall the wave ahead of its math
+        const bool pf = s + S - 1 < total;
+        const int pslot = (s + S - 1) % S;
+        const unsigned char* sw = smem + (s % S) * STAGE;
+        const unsigned char* sa = sw + BN * RB;
+        // fragments of sub-step j + 1 load while sub-step j's MFMAs run
+        bf16x8 fa[2][TN], fb[2][TM];
+        auto load_frags = [&](int j, int buf) {
+          const int c = 2 * j + half;
 #pragma unroll
           for (int t = 0; t < TM; ++t) {
-            const int mi = (j * TN + i) * TM + t;
-#pragma unroll
-            for (int q = 0; q < PER_STAGE; ++q)
-              if (q * MT / PER_STAGE == mi && pf) issue_one(pslot, q);
-            acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j & 1][i], fb[j & 1][t], acc[i][t], 0, 0, 0);
+            const int row = (wm * TM + t) * 32 + fr;
+            fb[buf][t] = *reinterpret_cast<const bf16x8*>(sa + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
           }
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < TN; ++i) {
+            const int row = (wn * TN + i) * 32 + fr;
+            fa[buf][i] = *reinterpret_cast<const bf16x8*>(sw + row * RB + 16 * (c ^ lds_swz_n<CPR>(row)));
+          }
+        };
+        constexpr int NJ = BK / 16;           // MFMA sub-steps per stage
+        constexpr int MT = NJ * TN * TM;      // MFMAs per stage
+        load_frags(0, 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (j + 1 < NJ) load_frags(j + 1, (j + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < TN; ++i)
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+              const int mi = (j * TN + i) * TM + t;
+#pragma unroll
+              for (int q = 0; q < PER_STAGE; ++q)
+                if (q * MT / PER_STAGE == mi && pf) issue_one(pslot, q);
+              acc[hh][i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j & 1][i], fb[j & 1][t], acc[hh][i][t], 0, 0, 0);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (pf) advance();
       }
-      if (pf) advance();
-    }
     // tile done: D[n][m], lane holds m = lane % 32 and four consecutive n per group
-    const int m0 = cc.mb * BM, n0 = cc.nb * BN;
+    const int m0 = cc.mb * BM;
 #pragma unroll
-    for (int t = 0; t < TM; ++t) {
-      const int m = m0 + (wm * TM + t) * 32 + fr;
-      if (GLU && m < cc.cnt) {
-        // elements 4q + u (q = 0, 1): W half of unit 8q + 4h + u of the 32-row
-        // tile's 16 units; elements 4q + 8 + u: the V half of the same unit
-        bf16_t* orow = out + (static_cast<int64_t>(cc.e) * C + m) * (N >> 1);
+    for (int hh = 0; hh < NH; ++hh) {
+      const int n0 = (cc.nb * NH + hh) * BN;
 #pragma unroll
-        for (int i = 0; i < TN; ++i) {
-          const int nt0 = n0 + (wn * TN + i) * 32;
-          if (nt0 < N) {
+      for (int t = 0; t < TM; ++t) {
+        const int m = m0 + (wm * TM + t) * 32 + fr;
+        if (GLU && m < cc.cnt) {
+          // elements 4q + u (q = 0, 1): W half of unit 8q + 4h + u of the 32-row
+          // tile's 16 units; elements 4q + 8 + u: the V half of the same unit
+          bf16_t* orow = out + (static_cast<int64_t>(cc.e) * C + m) * (N >> 1);
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              float h[4];
+          for (int i = 0; i < TN; ++i) {
+            const int nt0 = n0 + (wn * TN + i) * 32;
+            if (nt0 < N) {
 #pragma unroll
-              for (int u = 0; u < 4; ++u) h[u] = apply_act<ACT>(acc[i][t][4 * q + u]) * acc[i][t][4 * q + 8 + u];
-              uint2 v;
-              v.x = pack_bf16x2(h[0], h[1]);
-              v.y = pack_bf16x2(h[2], h[3]);
-              *reinterpret_cast<uint2*>(orow + (nt0 >> 1) + 8 * q + 4 * half) = v;
+              for (int q = 0; q < 2; ++q) {
+                float h[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) h[u] = apply_act<ACT>(acc[hh][i][t][4 * q + u]) * acc[hh][i][t][4 * q + 8 + u];
+                uint2 v;
+                v.x = pack_bf16x2(h[0], h[1]);
+                v.y = pack_bf16x2(h[2], h[3]);
+                *reinterpret_cast<uint2*>(orow + (nt0 >> 1) + 8 * q + 4 * half) = v;
+              }
             }
           }
-        }
-      } else if (m < cc.cnt) {
-        bf16_t* orow = out + (static_cast<int64_t>(cc.e) * C + m) * N;
+        } else if (m < cc.cnt) {
+          bf16_t* orow = out + (static_cast<int64_t>(cc.e) * C + m) * N;
 #pragma unroll
-        for (int i = 0; i < TN; ++i) {
-          const int nt0 = n0 + (wn * TN + i) * 32;
-          if (nt0 < N) {  // N % 32 == 0: a 32-column tile is wholly valid or not
+          for (int i = 0; i < TN; ++i) {
+            const int nt0 = n0 + (wn * TN + i) * 32;
+            if (nt0 < N) {  // N % 32 == 0: a 32-column tile is wholly valid or not
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int n = nt0 + 8 * q + 4 * half;
-              uint2 v;
-              v.x = pack_bf16x2(apply_act<ACT>(acc[i][t][4 * q]), apply_act<ACT>(acc[i][t][4 * q + 1]));
-              v.y = pack_bf16x2(apply_act<ACT>(acc[i][t][4 * q + 2]), apply_act<ACT>(acc[i][t][4 * q + 3]));
-              *reinterpret_cast<uint2*>(orow + n) = v;
+              for (int q = 0; q < 4; ++q) {
+                const int n = nt0 + 8 * q + 4 * half;
+                uint2 v;
+                v.x = pack_bf16x2(apply_act<ACT>(acc[hh][i][t][4 * q]), apply_act<ACT>(acc[hh][i][t][4 * q + 1]));
+                v.y = pack_bf16x2(apply_act<ACT>(acc[hh][i][t][4 * q + 2]), apply_act<ACT>(acc[hh][i][t][4 * q + 3]));
+                *reinterpret_cast<uint2*>(orow + n) = v;
+              }
             }
           }
         }
@@ -1407,15 +1423,16 @@ static hipError_t run_bf16(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
   return hipGetLastError();
 }
 
-template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT, bool GLU>
+template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT, bool GLU, bool PAIR = false>
 static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
                            const int32_t* count, int64_t C, int N, int K, hipStream_t s) {
-  auto kern = ffn_ring_bf16_kernel<TM, TN, WM, WN, S, BK, NTW, ACT, GLU>;
+  auto kern = ffn_ring_bf16_kernel<TM, TN, WM, WN, S, BK, NTW, ACT, GLU, PAIR>;
   constexpr int lds = ffn_ring_lds_bytes<TM, TN, WM, WN, S, BK>();
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
-  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32 * (PAIR ? 2 : 1);
+  if (PAIR && N % BN != 0) return hipErrorInvalidValue;
   const int64_t tiles = static_cast<int64_t>(E) * ((C + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
   const int64_t grid = std::min<int64_t>(tiles, 256);  // one persistent block per CU
@@ -1498,7 +1515,11 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // per CU, 192-row tiles (two per CU, 4 waves, a 4-stage ring of 32 KB stages)
 // balance the CUs and keep three stages of a cold weight stream in flight
 // (Switch-Base down-projection inside the forward: 128-130 us, against 137 us
-// for 384-row tiles with a 2-stage ring and 140 us for 256-row tiles).
+// for 384-row tiles with a 2-stage ring and 140 us for 256-row tiles), and a
+// CU's two tiles run as a pair, their stages alternating at each k-chunk, so
+// the second read of each activation chunk hits L2 (115.4 -> 109.5 us in the
+// kernel traces of the same forward steps; 384-row tiles with 32-k stages of
+// 28 KB instead: 12-15 us slower per step, 60 us with non-temporal weights).
 // Capacity > 160 (MFMA-bound: each weight tile is read by every row block of its
 // expert, so those loads stay temporal).  With a contraction of at least 2048 the
 // ping-pong kernel: 128 x 512 tiles (3-slot ring) where N holds at least four
@@ -1539,7 +1560,7 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
   if (p.C > 160) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (res_ok(p, N, K)) return run_res<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
-    return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+    return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU, true>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 128) return run_ring<4, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   return run_ring<5, 2, 1, 4, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
