@@ -151,6 +151,22 @@ def test_backward_matches_oracle(name):
             assert torch.equal(val, again[key]), f"{key} differs between calls"
 
 
+@pytest.mark.parametrize("name", ["switch_small_bf16", "rre_small_bf16", "geglu_wide_top1_bf16"])
+def test_backward_after_row_gathering_forward(name):
+    """Layers whose forward up-projection reads each slot's token row through
+    slot_token (bf16, capacity <= 64, d_model <= 768): moe_forward leaves the x_e
+    region of the workspace unwritten and moe_backward gathers it again.  With that
+    region filled with NaN before the forward, the gradients still match the oracle."""
+    wl = W.TEST_WORKLOADS[name]
+    print(f"[gpu] backward after a row-gathering forward {name}", flush=True)
+    inputs = W.make_inputs(wl)
+    ref = oracle.backward(wl, inputs, _oracle(wl, inputs), oracle.as_f64(make_dy(wl)))
+    dev = Dev(wl, inputs)
+    moe.workspace_view(dev.ws, dev.cfg, "x_e").view(torch.int16).fill_(0x7FC0)  # bf16 quiet NaN
+    got = dev.run_backward(make_dy(wl))
+    check_backward(wl, got, ref, name)
+
+
 @pytest.mark.parametrize("name", ["zipf_small_bf16", "rre_small_bf16", "tiny_switch_f32", "geglu_top2_bf16",
                                   "reglu_small_f32"])
 def test_sparse_clip(name):
