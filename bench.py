@@ -165,6 +165,12 @@ def main():
 
     # ---- per-kernel durations, live, with HIP events on the launch stream ----
     x_e = moe.workspace_view(ws, cfg, "x_e")
+    # moe_forward may leave x_e unwritten (its up-projection can gather the token rows
+    # itself): the calls below that read x_e from the workspace get it from moe_dispatch
+    # on the forward's own routing (same slots, so hidden and y_e stay the forward's)
+    moe.dispatch(cfg, x, moe.workspace_view(ws, cfg, "expert_idx"), moe.workspace_view(ws, cfg, "slot"),
+                 moe.workspace_view(ws, cfg, "expert_count"), moe.workspace_view(ws, cfg, "slot_token"), x_e,
+                 ws, stream)
     hidden = moe.workspace_view(ws, cfg, "hidden")
     y_e = moe.workspace_view(ws, cfg, "y_e")
     cnt_t = moe.workspace_view(ws, cfg, "expert_count")
