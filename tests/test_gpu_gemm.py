@@ -50,18 +50,48 @@ def _rows(n: int, rng) -> np.ndarray:
     return np.array(sorted(pick))
 
 
+# Capacity <= 64: the resident-activation kernel (K <= 768), the ring with paired
+# 192-row tiles (N a multiple of 384, at most 256 384-row units) and the 64 x 256
+# ring (other N), with empty experts, single rows and partly filled row blocks.
+CASES_64 = [
+    ("down ring 64x192 paired (K=1536, N=768), up resident (K=768)", 768, 1536, 40, 64, False),
+    ("GLU up ring 64x192 paired (K=1536, N=768), down resident (K=384)", 1536, 384, 40, 64, True),
+    ("up and down ring 64x256 (K=N=1024)", 1024, 1024, 40, 64, False),
+]
+
+
+def _workload(d, f, E, C, glu):
+    wl = W.Workload("gemm", T=E * C, d_model=d, d_ff=f, E=E, k=1, capacity_factor=1.0,
+                    act="gelu", dtype="bf16", glu=glu)
+    return wl, moe.config_for(wl)
+
+
 @pytest.mark.parametrize("label,d,f,E,C,glu", CASES, ids=[c[0] for c in CASES])
 def test_grouped_gemm_many_tiles(label, d, f, E, C, glu):
     print(f"[gpu] grouped GEMM {label}", flush=True)
-    wl = W.Workload("gemm", T=E * C, d_model=d, d_ff=f, E=E, k=1, capacity_factor=1.0,
-                    act="gelu", dtype="bf16", glu=glu)
-    cfg = moe.config_for(wl)
+    wl, cfg = _workload(d, f, E, C, glu)
     assert moe.capacity(cfg) == C
     counts = _counts(E, C, seed=E + C)
     # more tiles than the 256 persistent blocks in both projections (counted in 256 x 256 tiles)
     blocks = int(np.sum((counts + 255) // 256))
     assert blocks * (W.w1_rows(wl) // 256) > 256 and blocks * (d // 256) > 256
+    _check_gemm(label, wl, cfg, counts)
 
+
+@pytest.mark.parametrize("label,d,f,E,C,glu", CASES_64, ids=[c[0] for c in CASES_64])
+def test_grouped_gemm_capacity_64(label, d, f, E, C, glu):
+    print(f"[gpu] grouped GEMM {label}", flush=True)
+    wl, cfg = _workload(d, f, E, C, glu)
+    assert moe.capacity(cfg) == C
+    counts = _counts(E, C, seed=E + C)
+    assert (counts == 0).any() and (counts == 1).any() and (counts == C).any()
+    _check_gemm(label, wl, cfg, counts)
+
+
+def _check_gemm(label, wl, cfg, counts):
+    """moe_expert_up then moe_expert_down on seeded rows with the given per-expert counts;
+    sampled rows of H and y_e against the oracle's expert FFN."""
+    E, C, d, f, glu = wl.E, int(moe.capacity(cfg)), wl.d_model, wl.d_ff, wl.glu
     x = W.make_inputs(wl, with_weights=False)["x"].reshape(E, C, d)  # bf16 bits, dyadic
     w1 = torch.empty((E, W.w1_rows(wl), d), dtype=torch.bfloat16, device=DEV)
     w2 = torch.empty((E, d, f), dtype=torch.bfloat16, device=DEV)
