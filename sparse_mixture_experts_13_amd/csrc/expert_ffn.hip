@@ -1520,6 +1520,9 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // the second read of each activation chunk hits L2 (115.4 -> 109.5 us in the
 // kernel traces of the same forward steps; 384-row tiles with 32-k stages of
 // 28 KB instead: 12-15 us slower per step, 60 us with non-temporal weights).
+// Other N at capacity <= 64: 256-row tiles (8 waves, 3-stage ring), paired the
+// same way where N is a multiple of 512 (a Switch-like layer with d_model 1024,
+// d_ff 4096: up / down 226.5 / 236.8 -> 211.1 / 230.2 us, step 505 -> 483 us).
 // Capacity > 160 (MFMA-bound: each weight tile is read by every row block of its
 // expert, so those loads stay temporal).  With a contraction of at least 2048 the
 // ping-pong kernel: 128 x 512 tiles (3-slot ring) where N holds at least four
@@ -1561,6 +1564,8 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
   if (res_ok(p, N, K)) return run_res<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
     return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU, true>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C <= 64 && N % 512 == 0)
+    return run_ring<2, 1, 1, 8, 3, 64, true, ACT, GLU, true>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 128) return run_ring<4, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   return run_ring<5, 2, 1, 4, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);

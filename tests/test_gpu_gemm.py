@@ -52,11 +52,13 @@ def _rows(n: int, rng) -> np.ndarray:
 
 # Capacity <= 64: the resident-activation kernel (K <= 768), the ring with paired
 # 192-row tiles (N a multiple of 384, at most 256 384-row units) and the 64 x 256
-# ring (other N), with empty experts, single rows and partly filled row blocks.
+# ring (other N; paired where N is a multiple of 512), with empty experts, single
+# rows and partly filled row blocks.
 CASES_64 = [
     ("down ring 64x192 paired (K=1536, N=768), up resident (K=768)", 768, 1536, 40, 64, False),
     ("GLU up ring 64x192 paired (K=1536, N=768), down resident (K=384)", 1536, 384, 40, 64, True),
-    ("up and down ring 64x256 (K=N=1024)", 1024, 1024, 40, 64, False),
+    ("up and down ring 64x256 paired (K=N=1024)", 1024, 1024, 40, 64, False),
+    ("up ring 64x256 (N=1216), down ring 64x256 paired (K=1216, N=1024)", 1024, 1216, 40, 64, False),
 ]
 
 
