@@ -1522,7 +1522,11 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // 28 KB instead: 12-15 us slower per step, 60 us with non-temporal weights).
 // Other N at capacity <= 64: 256-row tiles (8 waves, 3-stage ring), paired the
 // same way where N is a multiple of 512 (a Switch-like layer with d_model 1024,
-// d_ff 4096: up / down 226.5 / 236.8 -> 211.1 / 230.2 us, step 505 -> 483 us).
+// d_ff 4096: up / down 226.5 / 236.8 -> 211.1 / 230.2 us, step 505 -> 483 us),
+// and likewise the 128 x 256 tiles at capacity <= 128 (E = 64, capacity 128,
+// d_ff 4096: up-projection 123.7 -> 117.3 us).  Pairs are taken only where they
+// still number at least 256: with half as many units as CUs, that layer's
+// down-projection (128 units) took 174.6 us against 137.7 unpaired.
 // Capacity > 160 (MFMA-bound: each weight tile is read by every row block of its
 // expert, so those loads stay temporal).  With a contraction of at least 2048 the
 // ping-pong kernel: 128 x 512 tiles (3-slot ring) where N holds at least four
@@ -1562,11 +1566,21 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
   if (pp_ok && p.C > 160 && K >= 2048) return run_pp<4, 2, 4, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C > 160) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (res_ok(p, N, K)) return run_res<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256)
-    return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU, true>(p.E, A, W, out, count, p.C, N, K, s);
-  if (p.C <= 64 && N % 512 == 0)
+  // pairing a block's two column tiles halves the work units: only where the pairs
+  // still cover the 256 CUs
+  auto pairs = [&](int bm, int bn) {
+    return N % (2 * bn) == 0 && static_cast<int64_t>(p.E) * ((p.C + bm - 1) / bm) * (N / (2 * bn)) >= 256;
+  };
+  if (p.C <= 64 && N % 384 == 0 && static_cast<int64_t>(p.E) * (N / 384) <= 256) {
+    if (pairs(64, 192))
+      return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU, true>(p.E, A, W, out, count, p.C, N, K, s);
+    return run_ring<1, 3, 2, 2, 4, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  }
+  if (p.C <= 64 && pairs(64, 256))
     return run_ring<2, 1, 1, 8, 3, 64, true, ACT, GLU, true>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 64) return run_ring<2, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (p.C <= 128 && pairs(128, 256))
+    return run_ring<4, 1, 1, 8, 3, 64, true, ACT, GLU, true>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C <= 128) return run_ring<4, 1, 1, 8, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   return run_ring<5, 2, 1, 4, 3, 64, true, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
 }

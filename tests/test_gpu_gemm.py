@@ -50,15 +50,21 @@ def _rows(n: int, rng) -> np.ndarray:
     return np.array(sorted(pick))
 
 
-# Capacity <= 64: the resident-activation kernel (K <= 768), the ring with paired
-# 192-row tiles (N a multiple of 384, at most 256 384-row units) and the 64 x 256
-# ring (other N; paired where N is a multiple of 512), with empty experts, single
-# rows and partly filled row blocks.
-CASES_64 = [
-    ("down ring 64x192 paired (K=1536, N=768), up resident (K=768)", 768, 1536, 40, 64, False),
-    ("GLU up ring 64x192 paired (K=1536, N=768), down resident (K=384)", 1536, 384, 40, 64, True),
-    ("up and down ring 64x256 paired (K=N=1024)", 1024, 1024, 40, 64, False),
-    ("up ring 64x256 (N=1216), down ring 64x256 paired (K=1216, N=1024)", 1024, 1216, 40, 64, False),
+# Capacity <= 128: the resident-activation kernel (capacity <= 64, K <= 768), the
+# ring with 192-row tiles (N a multiple of 384, at most 256 384-row units) and the
+# 64 x 256 and 128 x 256 rings (other N), each with a block's two column tiles
+# paired where the pairs number at least 256 (E = 256 here) and unpaired below
+# that (E = 40), with empty experts, single rows and partly filled row blocks.
+CASES_SMALL_C = [
+    ("E=40: down ring 64x192 (K=1536, N=768), up resident (K=768)", 768, 1536, 40, 64, False),
+    ("E=40: GLU up ring 64x192 (K=1536, N=768), down resident (K=384)", 1536, 384, 40, 64, True),
+    ("E=40: up and down ring 64x256 (K=N=1024)", 1024, 1024, 40, 64, False),
+    ("E=40: up ring 64x256 (N=1216), down ring 64x256 (K=1216, N=1024)", 1024, 1216, 40, 64, False),
+    ("E=256: down ring 64x192 paired (K=1024, N=384), up resident (K=384)", 384, 1024, 256, 64, False),
+    ("E=256: up and down ring 64x256 paired (K=N=1024)", 1024, 1024, 256, 64, False),
+    ("E=256: GLU up ring 64x256 paired (K=1024, N=1024), down resident (K=512)", 1024, 512, 256, 64, True),
+    ("E=256: up and down ring 128x256 paired, capacity 128", 1024, 512, 256, 128, False),
+    ("E=40: up and down ring 128x256, capacity 100", 1024, 1024, 40, 100, False),
 ]
 
 
@@ -80,8 +86,8 @@ def test_grouped_gemm_many_tiles(label, d, f, E, C, glu):
     _check_gemm(label, wl, cfg, counts)
 
 
-@pytest.mark.parametrize("label,d,f,E,C,glu", CASES_64, ids=[c[0] for c in CASES_64])
-def test_grouped_gemm_capacity_64(label, d, f, E, C, glu):
+@pytest.mark.parametrize("label,d,f,E,C,glu", CASES_SMALL_C, ids=[c[0] for c in CASES_SMALL_C])
+def test_grouped_gemm_small_capacity(label, d, f, E, C, glu):
     print(f"[gpu] grouped GEMM {label}", flush=True)
     wl, cfg = _workload(d, f, E, C, glu)
     assert moe.capacity(cfg) == C
