@@ -18,7 +18,8 @@
  * Conventions shared by every entry point
  *   - Pointers named x, w_r, bias, group_id, w1, w2, y, expert_idx, gate, slot,
  *     expert_count, slot_token, x_e, y_e and ws are DEVICE pointers owned by the
- *     caller.  The library allocates nothing and keeps no state between calls.
+ *     caller.  The library allocates nothing and keeps no state between calls
+ *     (moe_forward_noalloc's static scratch aside, see there).
  *     `cfg` is a HOST pointer, read during the call only.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     All GPU work is enqueued on it; no call synchronises the host.  Results
@@ -48,8 +49,8 @@ extern "C" {
 #endif
 
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
-/* Expert activation.  RELU / GELU: the plain FFN act(x W1) W2 (GELU with the
- * exact erf).  REGLU / GEGLU: the gated-linear-unit FFN of the MosaicBERT review
+/* Expert activation.  RELU / GELU: the plain FFN act(x W1) W2 (GELU in its erf
+ * form, x * (1 + erf(x / sqrt 2)) / 2, with erf evaluated within 4.3e-7).  REGLU / GEGLU: the gated-linear-unit FFN of the MosaicBERT review
  * (methodology: gated linear units in the feed-forward layer),
  * (act(x W) * (x V)) W2 with act ReLU / GELU, the product elementwise; W and V
  * are stored stacked in w1 (see moe_expert_ffn), so w1 has 2 * d_ff rows. */
@@ -73,7 +74,7 @@ typedef struct moe_config {
   int32_t route;           /* moe_route                                              */
   int32_t n_groups;        /* RRE: expert groups (experts g*E/n_groups ... next)     */
   uint64_t rre_seed;       /* RRE: SplitMix64 seed                                   */
-  int32_t act;             /* moe_act: ReLU, GELU (exact erf), or their GLU forms   */
+  int32_t act;             /* moe_act: ReLU, GELU (erf form), or their GLU forms    */
   int32_t dtype;           /* moe_dtype of x, w1, w2, x_e, y_e, y                    */
 } moe_config;
 
