@@ -792,17 +792,19 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
 // `aux` at the output position (the backward's dZ).
 // ---------------------------------------------------------------------------
 // TM x TN MFMA tiles per wave (activation, weight), R ring slots of 32-k stages.
-template <int TM, int TN, int R>
+template <int TM, int TN, int R, int BK = 32>
 __host__ __device__ constexpr int ffn_pp_lds_bytes() {
-  return R * (2 * TM * 32 + 4 * TN * 32) * 32 * 2 + (2 * kMaxE + 1) * 4;
+  return R * (2 * TM * 32 + 4 * TN * 32) * BK * 2 + (2 * kMaxE + 1) * 4;
 }
 
-template <int TM, int TN, int R, int ACT, bool GLU, bool BT = false, int EPI = 0>
+template <int TM, int TN, int R, int ACT, bool GLU, bool BT = false, int EPI = 0, int BK = 32>
 __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
     const int32_t* __restrict__ count, int E, int64_t C, int N, int K, const bf16_t* __restrict__ aux) {
   static_assert(!(BT && GLU) && (EPI == 0 || (EPI == 1 && !GLU)), "operand and epilogue forms");
-  constexpr int BM = 2 * TM * 32, BN = 4 * TN * 32, BK = 32;
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  constexpr int BM = 2 * TM * 32, BN = 4 * TN * 32;
+  constexpr int NJ = BK / 16;            // MFMA sub-steps per stage
   constexpr int KRB = BN * 2;            // BT: bytes per k row of the weight stage tile
   constexpr int RB = BK * 2;             // LDS row bytes
   constexpr int CPR = BK / 8;            // 16-byte chunks per row
@@ -890,7 +892,7 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
     for (int q = 0; q < WL; ++q) {
       const int p = (wave * WL + q) * 64 + lane;
       uint32_t off;
-      if constexpr (BT) {  // 16-byte chunk p of the [32][BN] tile: k row p / (BN / 8)
+      if constexpr (BT) {  // 16-byte chunk p of the [BK][BN] tile: k row p / (BN / 8)
         const int kr = p / (BN / 8);
         const int c = (p % (BN / 8)) ^ (4 * (kr & 3));
         off = static_cast<uint32_t>(lk * BK + kr) * N + min(lc.nb * BN + c * 8, N - 8);
@@ -951,9 +953,9 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
     // memory phase
     const unsigned char* sw = smem + (s % R) * STAGE;
     const unsigned char* sa = sw + BN * RB;
-    bf16x8 fa[2][TN], fb[2][TM];
+    bf16x8 fa[NJ][TN], fb[NJ][TM];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int c = 2 * j + half;
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
@@ -989,7 +991,7 @@ __global__ __launch_bounds__(512) void ffn_pp_bf16_kernel(
     barrier();
     // MFMA phase
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -1457,11 +1459,11 @@ static hipError_t run_res(int E, const bf16_t* A, const bf16_t* W, bf16_t* out, 
   return hipGetLastError();
 }
 
-template <int TM, int TN, int R, int ACT, bool GLU, bool BT = false, int EPI = 0>
+template <int TM, int TN, int R, int ACT, bool GLU, bool BT = false, int EPI = 0, int BK = 32>
 static hipError_t run_pp(int E, const bf16_t* A, const bf16_t* W, bf16_t* out, const int32_t* count,
                          int64_t C, int N, int K, hipStream_t s, const bf16_t* aux = nullptr) {
-  auto kern = ffn_pp_bf16_kernel<TM, TN, R, ACT, GLU, BT, EPI>;
-  constexpr int lds = ffn_pp_lds_bytes<TM, TN, R>();
+  auto kern = ffn_pp_bf16_kernel<TM, TN, R, ACT, GLU, BT, EPI, BK>;
+  constexpr int lds = ffn_pp_lds_bytes<TM, TN, R, BK>();
   constexpr int BM = 2 * TM * 32, BN = 4 * TN * 32;
   static_assert(lds <= 160 * 1024, "LDS budget");
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1529,13 +1531,16 @@ static hipError_t run_f32(int E, const float* A, const float* W, float* out, con
 // down-projection (128 units) took 174.6 us against 137.7 unpaired.
 // Capacity > 160 (MFMA-bound: each weight tile is read by every row block of its
 // expert, so those loads stay temporal).  With a contraction of at least 2048 the
-// ping-pong kernel: 128 x 512 tiles (3-slot ring) where N holds at least four
-// 512-row column blocks, so that a partly filled last row block wastes at most
-// 127 rows (large Zipf layer, capacity 320, counts 162..320: 3.24 / 3.12 ms up /
-// down against 3.47 / 3.25 ms for 256 x 256 tiles and 3.70 / 3.46 ms for the
-// LDS-tiled 128 x 128 kernel), else 256 x 256 tiles (X-MoE top-2
-// down-projection, N = 1024, K = 4096: 380 us against 451 us for 128 x 512,
-// whose 578 long tiles balance poorly over 256 CUs, and 402 us for the ring).
+// ping-pong kernel with 128 x 256 tiles and 64-k stages (3 slots of 48 KB).  The
+// stream of a CU into LDS is bound by the L2 read requests it can keep in flight
+// (rocprofv3: 80-90 on average in every grouped GEMM, at 400-450 cycles of L2
+// latency here), so a stage that reads whole 128-byte rows moves twice the bytes
+// per request of the 32-k stages' 64-byte pieces: against 128 x 512 tiles with
+// 32-k stages (large Zipf layer, capacity 320) up / down 2.91 / 2.80 ms instead of
+// 3.08 / 3.09 ms, against 256 x 256 with 32-k stages (X-MoE top-2
+// down-projection, N = 1024, K = 4096) 327 instead of 356 us, same output bits.
+// 128-row blocks also waste at most 127 rows of a partly filled last row block
+// (X-MoE pads its 32 768 served rows by 26% in 256-row blocks).
 // Shorter contractions, where a tile's epilogue is a larger share of its time:
 // the ring with 256 x 256 tiles, 8 waves of 4 x 2 MFMA tiles and a 2-stage ring
 // of 64 KB stages (X-MoE up-projection, K = 1024: 410 us against 443 us for
@@ -1561,9 +1566,8 @@ static hipError_t gemm_bf16(const Plan& p, const bf16_t* A, const bf16_t* W, bf1
   if (int64_t(N) * K >= lim || p.C * K >= lim)
     return run_bf16<128, 128, 2, 2, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   const bool pp_ok = int64_t(N) * K * 2 < (int64_t(1) << 31) && p.C * K * 2 < (int64_t(1) << 31);
-  if (pp_ok && p.C > 160 && K >= 2048 && N >= 2048)
-    return run_pp<2, 4, 3, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
-  if (pp_ok && p.C > 160 && K >= 2048) return run_pp<4, 2, 4, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
+  if (pp_ok && p.C > 160 && K >= 2048)
+    return run_pp<2, 2, 3, ACT, GLU, false, 0, 64>(p.E, A, W, out, count, p.C, N, K, s);
   if (p.C > 160) return run_ring<4, 2, 2, 4, 2, 64, false, ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   if (res_ok(p, N, K)) return run_res<ACT, GLU>(p.E, A, W, out, count, p.C, N, K, s);
   // pairing a block's two column tiles halves the work units: only where the pairs
