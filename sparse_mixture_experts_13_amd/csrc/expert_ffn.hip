@@ -763,16 +763,17 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
 // Ping-pong grouped GEMM for large capacities, where a tile re-reads its weight
 // rows for several row blocks and the MFMA pipe, not HBM, sets the pace.
 //
-// Block tile: BM = 64 TM activation rows x BN = 128 TN weight rows (256 x 256 or
-// 128 x 512), persistent blocks of 8 waves in two groups of four (waves w and
+// Block tile: BM = 64 TM activation rows x BN = 128 TN weight rows (128 x 256
+// with 64-k stages in the forward; 256 x 256 or 128 x 512 with 32-k stages in
+// the BT form below), persistent blocks of 8 waves in two groups of four (waves w and
 // w + 4 share a SIMD).  Wave (g, wn) owns activation rows g BM / 2 .. and weight
 // rows wn BN / 4 .. of the tile: TM x TN MFMA tiles of 32 x 32.  The k loop runs
-// in 32-k stages through an R-slot direct-to-LDS ring, and every stage has two
+// in BK-k stages through an R-slot direct-to-LDS ring, and every stage has two
 // phases separated by block barriers:
 //   * memory phase: read the wave's fragments of the stage from LDS, issue its
 //     direct-to-LDS loads of the stage R - 1 ahead, wait for its own loads of
 //     the next stage;
-//   * MFMA phase: 16 MFMAs on the fragments in registers (and the tile's
+//   * MFMA phase: (BK / 16) TM TN MFMAs on the fragments in registers (and the tile's
 //     epilogue after its last stage).
 // Group 1 runs one phase behind group 0, so on every SIMD one wave issues
 // MFMAs while the other feeds LDS and memory: the matrix pipe never waits for
@@ -791,7 +792,7 @@ __global__ __launch_bounds__(512) void ffn_res_bf16_kernel(const bf16_t* __restr
 // 8-byte bank slots.  EPI 1 multiplies the product by act'(z), z read from
 // `aux` at the output position (the backward's dZ).
 // ---------------------------------------------------------------------------
-// TM x TN MFMA tiles per wave (activation, weight), R ring slots of 32-k stages.
+// TM x TN MFMA tiles per wave (activation, weight), R ring slots of BK-k stages.
 template <int TM, int TN, int R, int BK = 32>
 __host__ __device__ constexpr int ffn_pp_lds_bytes() {
   return R * (2 * TM * 32 + 4 * TN * 32) * BK * 2 + (2 * kMaxE + 1) * 4;

@@ -24,12 +24,15 @@ pytestmark = pytest.mark.gpu
 
 # (label, d_model, d_ff, E, capacity, glu); the kernel each projection takes
 # follows from the capacity (> 160), the contraction K and the output rows N.
+# The ping-pong tiles are 128 x 256 with 64-k stages: counts on both sides of 128 and 256
+# give partly filled last row blocks, N = 2112 a 64-row last column tile, K = 2112 an odd
+# number (33) of stages.
 CASES = [
-    ("up ring 256x256 (K=1024), down ping-pong 256x256 (K=2048, N=1024)", 1024, 2048, 40, 600, False),
-    ("GLU up ring 256x256 (N=4096), down ping-pong 256x256", 1024, 2048, 40, 600, True),
-    ("up and down ping-pong 128x512 (K=N=2048)", 2048, 2048, 40, 300, False),
-    ("GLU up ping-pong 128x512 (K=N=2048), down ring 256x256 (K=1024)", 2048, 1024, 40, 300, True),
-    ("up and down ping-pong 128x512, N = 2112 (last column tile 64 rows), K = 2112", 2048, 2112, 40, 300, False),
+    ("up ring 256x256 (K=1024), down ping-pong 128x256 (K=2048, N=1024)", 1024, 2048, 40, 600, False),
+    ("GLU up ring 256x256 (N=4096), down ping-pong 128x256", 1024, 2048, 40, 600, True),
+    ("up and down ping-pong 128x256 (K=N=2048)", 2048, 2048, 40, 300, False),
+    ("GLU up ping-pong 128x256 (K=N=2048), down ring 256x256 (K=1024)", 2048, 1024, 40, 300, True),
+    ("up and down ping-pong 128x256, N = 2112 (last column tile 64 rows), K = 2112", 2048, 2112, 40, 300, False),
 ]
 
 
@@ -80,7 +83,8 @@ def test_grouped_gemm_many_tiles(label, d, f, E, C, glu):
     wl, cfg = _workload(d, f, E, C, glu)
     assert moe.capacity(cfg) == C
     counts = _counts(E, C, seed=E + C)
-    # more tiles than the 256 persistent blocks in both projections (counted in 256 x 256 tiles)
+    # more tiles than the 256 persistent blocks in both projections (counted in 256 x 256 tiles,
+    # so also in the smaller ping-pong tiles)
     blocks = int(np.sum((counts + 255) // 256))
     assert blocks * (W.w1_rows(wl) // 256) > 256 and blocks * (d // 256) > 256
     _check_gemm(label, wl, cfg, counts)
