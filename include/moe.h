@@ -93,7 +93,8 @@ int64_t moe_workspace_bytes(const moe_config* cfg);
 
 /* Regions of the workspace that moe_forward fills, for inspection after the call.
  * One exception: on bfloat16 layers with capacity <= 64, d_model <= 768 and
- * E <= 512 the up-projection reads each slot's token row from x itself
+ * E <= 512, and on bfloat16 layers with capacity > 160 and d_model < 2048, the
+ * up-projection inside moe_forward reads each slot's token row from x itself
  * (through slot_token), and moe_forward leaves MOE_WS_X_E unwritten there
  * (moe_dispatch always writes its x_e; moe_backward gathers the rows again). */
 typedef enum {

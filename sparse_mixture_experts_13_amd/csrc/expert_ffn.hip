@@ -236,10 +236,19 @@ __host__ __device__ constexpr int ffn_ring_lds_bytes() {
 // their weight rows at each k-chunk (k-chunk i of half 0, then of half 1), each
 // stage carrying the row block's k-chunk i, so the second copy of every
 // activation chunk is read while the first is still in L2.
-template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT, bool GLU, bool PAIR = false>
+// TOK (the whole-layer forward, two ring slots): A is the token rows x [T][K] and
+// row s of expert e is x[tok[e C + s]], so the dispatch copies no rows.  Each lane
+// keeps the token of each of its activation-load rows for the loader's current
+// tile, loaded when the loader moves to the tile, at the end of a stage: with two
+// slots every stage starts by waiting for all loads, so those tokens have landed
+// before the next stage's loads use them.
+template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT, bool GLU, bool PAIR = false,
+          bool TOK = false>
 __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, bf16_t* __restrict__ out,
-    const int32_t* __restrict__ count, int E, int64_t C, int N, int K) {
+    const int32_t* __restrict__ count, int E, int64_t C, int N, int K,
+    const int32_t* __restrict__ tok = nullptr) {
+  static_assert(!TOK || S == 2, "token-row loads rely on the two-slot ring's full wait per stage");
   constexpr int NW = WM * WN;
   constexpr int NH = PAIR ? 2 : 1;  // column tiles per unit
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
@@ -365,6 +374,20 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
   seek(lc, v0);
   cc = lc;
   int lk = 0, lh = 0;  // loader: k-chunk and column half of the stage it issues next
+  // TOK: token of this lane's row of activation load q in the loader's tile
+  int tokv[AL];
+  auto load_tok = [&]() {
+    if constexpr (TOK) {
+      if (lc.e < E) {
+#pragma unroll
+        for (int qa = 0; qa < AL; ++qa) {
+          const int row = ((wave * AL + qa) * 64 + lane) / CPR;
+          tokv[qa] = tok[static_cast<int64_t>(lc.e) * C + min(lc.mb * BM + row, lc.cnt - 1)];
+        }
+      }
+    }
+  };
+  load_tok();
   // Loads use a block-uniform per-expert base plus 32-bit lane offsets.
   // issue_one(slot, q) issues the q-th of the PER_STAGE direct-to-LDS
   // instructions of the loader's current stage; advance() moves to the next.
@@ -383,12 +406,17 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
                                        NTW ? 2 : 0);
     } else {
       const int qa = q - WL;
-      const bf16_t* Ae = A + static_cast<int64_t>(lc.e) * C * K;
       const int p = (wave * AL + qa) * 64 + lane;
       const int row = p / CPR;
       const int c = (p % CPR) ^ lds_swz_n<CPR>(row);
-      const uint32_t off = static_cast<uint32_t>(min(lc.mb * BM + row, lc.cnt - 1)) * K + lk * BK + c * 8;
-      __builtin_amdgcn_global_load_lds(Ae + off, (lds_void*)(base + BN * RB + (wave * AL + qa) * 1024),
+      const bf16_t* src;
+      if constexpr (TOK) {
+        src = A + static_cast<int64_t>(tokv[qa]) * K + lk * BK + c * 8;
+      } else {
+        const bf16_t* Ae = A + static_cast<int64_t>(lc.e) * C * K;
+        src = Ae + static_cast<uint32_t>(min(lc.mb * BM + row, lc.cnt - 1)) * K + lk * BK + c * 8;
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + BN * RB + (wave * AL + qa) * 1024),
                                        16, 0, 0);
     }
   };
@@ -398,6 +426,7 @@ __global__ __launch_bounds__(WM * WN * 64) void ffn_ring_bf16_kernel(
     if (++lk == KS) {
       lk = 0;
       step(lc);
+      load_tok();
     }
   };
   auto issue = [&](int slot) {
@@ -1426,10 +1455,12 @@ static hipError_t run_bf16(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
   return hipGetLastError();
 }
 
-template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT, bool GLU, bool PAIR = false>
+template <int TM, int TN, int WM, int WN, int S, int BK, bool NTW, int ACT, bool GLU, bool PAIR = false,
+          bool TOK = false>
 static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
-                           const int32_t* count, int64_t C, int N, int K, hipStream_t s) {
-  auto kern = ffn_ring_bf16_kernel<TM, TN, WM, WN, S, BK, NTW, ACT, GLU, PAIR>;
+                           const int32_t* count, int64_t C, int N, int K, hipStream_t s,
+                           const int32_t* tok = nullptr) {
+  auto kern = ffn_ring_bf16_kernel<TM, TN, WM, WN, S, BK, NTW, ACT, GLU, PAIR, TOK>;
   constexpr int lds = ffn_ring_lds_bytes<TM, TN, WM, WN, S, BK>();
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1440,7 +1471,7 @@ static hipError_t run_ring(int E, const bf16_t* A, const bf16_t* W, bf16_t* out,
   if (tiles == 0) return hipSuccess;
   const int64_t grid = std::min<int64_t>(tiles, 256);  // one persistent block per CU
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(WM * WN * 64), lds, s, A, W,
-                     out, count, E, C, N, K);
+                     out, count, E, C, N, K, tok);
   return hipGetLastError();
 }
 
@@ -1556,8 +1587,15 @@ static bool res_ok(const Plan& p, int64_t N, int64_t K) {
   return N * K < lim && p.C * K < lim && p.C <= 64 && K <= kResMaxK && p.E <= kMaxE;
 }
 
+// The up-projection of gemm_bf16 on the two-slot 256 x 256 ring (capacity > 160,
+// contraction below the ping-pong kernel's 2048, 32-bit panel offsets).
+static bool ring2_up(const Plan& p) {
+  const int64_t lim = int64_t(1) << 32, N = p.w1_rows(), K = p.d;
+  return N * K < lim && p.C * K < lim && p.C > 160 && K < 2048;
+}
+
 bool up_reads_token_rows(const Plan& p) {
-  return p.dtype == 1 && p.C > 0 && p.T > 0 && res_ok(p, p.w1_rows(), p.d);
+  return p.dtype == 1 && p.C > 0 && p.T > 0 && (res_ok(p, p.w1_rows(), p.d) || ring2_up(p));
 }
 
 template <int ACT, bool GLU = false>
@@ -1688,12 +1726,27 @@ hipError_t launch_expert_ffn_rows(const Plan& p, const void* x, const int32_t* s
   bf16_t* h = static_cast<bf16_t*>(hidden);
   const int d = static_cast<int>(p.d), f = static_cast<int>(p.f);
   hipError_t err;
-  if (p.glu)
+  if (ring2_up(p)) {
+    // the ring kernel of gemm_bf16 for this shape, its activation rows read from x
+    if (p.glu)
+      err = p.act == 0
+                ? run_ring<4, 2, 2, 4, 2, 64, false, 0, true, false, true>(p.E, xr, w, h, expert_count, p.C,
+                                                                         2 * f, d, s, slot_token)
+                : run_ring<4, 2, 2, 4, 2, 64, false, 1, true, false, true>(p.E, xr, w, h, expert_count, p.C,
+                                                                         2 * f, d, s, slot_token);
+    else
+      err = p.act == 0
+                ? run_ring<4, 2, 2, 4, 2, 64, false, 0, false, false, true>(p.E, xr, w, h, expert_count, p.C,
+                                                                          f, d, s, slot_token)
+                : run_ring<4, 2, 2, 4, 2, 64, false, 1, false, false, true>(p.E, xr, w, h, expert_count, p.C,
+                                                                          f, d, s, slot_token);
+  } else if (p.glu) {
     err = p.act == 0 ? run_res<0, true>(p.E, xr, w, h, expert_count, p.C, 2 * f, d, s, slot_token)
                      : run_res<1, true>(p.E, xr, w, h, expert_count, p.C, 2 * f, d, s, slot_token);
-  else
+  } else {
     err = p.act == 0 ? run_res<0, false>(p.E, xr, w, h, expert_count, p.C, f, d, s, slot_token)
                      : run_res<1, false>(p.E, xr, w, h, expert_count, p.C, f, d, s, slot_token);
+  }
   if (err != hipSuccess) return err;
   return launch_expert_down(p, hidden, expert_count, w2, y_e, s);
 }

@@ -151,12 +151,14 @@ def test_backward_matches_oracle(name):
             assert torch.equal(val, again[key]), f"{key} differs between calls"
 
 
-@pytest.mark.parametrize("name", ["switch_small_bf16", "rre_small_bf16", "geglu_wide_top1_bf16"])
+@pytest.mark.parametrize("name", ["switch_small_bf16", "rre_small_bf16", "geglu_wide_top1_bf16",
+                                  "xmoe_small_bf16", "geglu_top2_bf16"])
 def test_backward_after_row_gathering_forward(name):
     """Layers whose forward up-projection reads each slot's token row through
-    slot_token (bf16, capacity <= 64, d_model <= 768): moe_forward leaves the x_e
-    region of the workspace unwritten and moe_backward gathers it again.  With that
-    region filled with NaN before the forward, the gradients still match the oracle."""
+    slot_token (bf16 with capacity <= 64 and d_model <= 768, or capacity > 160 and
+    d_model < 2048): moe_forward leaves the x_e region of the workspace unwritten and
+    moe_backward gathers it again.  With that region filled with NaN before the
+    forward, the gradients still match the oracle."""
     wl = W.TEST_WORKLOADS[name]
     print(f"[gpu] backward after a row-gathering forward {name}", flush=True)
     inputs = W.make_inputs(wl)
