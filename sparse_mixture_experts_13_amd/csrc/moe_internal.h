@@ -61,8 +61,9 @@ hipError_t launch_expert_ffn(const Plan& p, const void* x_e, const int32_t* expe
 hipError_t launch_expert_up(const Plan& p, const void* x_e, const int32_t* expert_count,
                             const void* w1, void* hidden, hipStream_t s);
 // True where the up-projection can read each slot's activation row from the
-// token rows x through slot_token instead of from x_e (the resident-activation
-// GEMM: bf16, capacity <= 64, d_model <= 768, E <= 512).
+// token rows x through slot_token instead of from x_e: the resident-activation
+// GEMM (bf16, capacity <= 64, d_model <= 768, E <= 512) and the two-slot ring
+// (bf16, capacity > 160, d_model < 2048).
 bool up_reads_token_rows(const Plan& p);
 // The expert FFN of launch_expert_ffn with the up-projection reading x[slot_token]
 // (only where up_reads_token_rows holds; hipErrorInvalidValue elsewhere).
